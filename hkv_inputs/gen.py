@@ -192,3 +192,36 @@ def all_inputs(cfg: HkvConfig, seed: int):
                 k, v, q = stream_inputs(cfg, seed, l, b, h, bias)
                 ks.append(k); vs.append(v); qs.append(q)
     return np.stack(ks), np.stack(vs), np.stack(qs)
+
+
+def _floyd_vec(words: np.ndarray, lo_range: int, count: int) -> np.ndarray:
+    """Vectorised `_floyd` over rows of `words` ([n, >=count] uint)."""
+    n = words.shape[0]
+    chosen = np.zeros((n, count), dtype=np.int64)
+    for i, j in enumerate(range(lo_range - count, lo_range)):
+        t = (words[:, i].astype(np.int64)) % (j + 1)
+        dup = (chosen[:, :i] == t[:, None]).any(axis=1) if i else np.zeros(n, bool)
+        chosen[:, i] = np.where(dup, j, t)
+    return chosen
+
+
+def anchors_all(cfg: HkvConfig, seed: int) -> np.ndarray:
+    """int32 [S, 4]: `anchors(cfg, seed, s)` for every stream."""
+    k0, k1 = _key(cfg, seed)
+    S = cfg.S
+    ss, kk = np.meshgrid(np.arange(S), np.arange(4), indexing="ij")
+    w = philox4x32_10(kk, ss, TAG_ANCHOR, 0, k0, k1)[0]          # [S, 4]
+    if cfg.anchor_mode == "prefill":
+        out = _floyd_vec(w, cfg.P - 32, 4)
+    else:
+        a0 = (w[:, 0].astype(np.int64)) % (cfg.P - 40 + 1)
+        rest = _floyd_vec(w[:, 1:], cfg.N - 32 - 1, 3)
+        rest = np.where(rest < a0[:, None], rest, rest + 1)
+        out = np.concatenate([a0[:, None], rest], axis=1)
+    return np.sort(out, axis=1).astype(np.int32)
+
+
+def local_flags(cfg: HkvConfig, seed: int) -> np.ndarray:
+    """uint8 [S]: 1 where the stream uses the locality-biased query generator."""
+    bias = head_bias(cfg, seed)                       # [L, H]
+    return np.repeat(bias[:, None, :], cfg.batch, axis=1).reshape(-1).astype(np.uint8)

@@ -1,0 +1,178 @@
+/*
+ * hkv.h — C ABI of the HeadKV decode-time path on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "Head-Aware Key-Value Compression for Efficient
+ * Autoregressive Image Generation", gist.science technical summaries, section
+ * "Methodology"):
+ *   step 1  the cache is prefilled without compression;
+ *   step 2  once it reaches a predefined length every attention head is
+ *           classified once: the current query's attention is accumulated
+ *           backward from the current position until it reaches tau (0.9);
+ *           fewer tokens than the local window -> Local, otherwise Global;
+ *   step 3  Local heads keep a sliding window of the newest tokens; Global heads
+ *           keep a budget enforced by Stratified Token Eviction (STE): the
+ *           history is split by distance into disjoint near and far subsets,
+ *           each scored from past queries, and the lowest-scoring tokens of each
+ *           subset are evicted (M/2 + M/2).
+ *   Budgets are asymmetric (section "Key contributions", item 2): compact for
+ *   Local heads, larger for Global heads, at a total of rho of the full cache.
+ *
+ * Readings this library implements where the pages are silent (all are
+ * checked against an independent CPU oracle):
+ *   - attention: single-query softmax, logits q.k/sqrt(d), one KV head per head;
+ *     at decode step t token t is appended first, then attended;
+ *   - classification query: position P-1 over positions 0..P-1; count n = the
+ *     smallest k with (mass of the k newest) >= tau; Local iff n < w;
+ *   - budget per (layer, sequence): A = floor(N*rho_num/rho_den), Local heads w
+ *     slots, Global heads B_g = floor((H*A - n_L*w) / n_G), capacity B_g + M;
+ *   - score of a slot = sum of the softmax probabilities it received from the
+ *     last W queries (W = w_obs = M); the W newest tokens are not candidates;
+ *     near: W <= t-pos < D, far: t-pos >= D; quotas floor(E/2) near and the
+ *     rest far, a short subset gives all it has; order (score, position);
+ *   - layout: Local slot = pos mod w; Global slots compact, evicted slots below
+ *     B_g refilled in ascending order by the surviving tail slots; at
+ *     classification an over-long Global prefix is reduced by STE with the W
+ *     last prefill queries, survivors in ascending position order.
+ *
+ * Conventions (every entry point):
+ *   - Streams: s = (l*batch + b)*heads + h.  Calls on a stream range take
+ *     [s_begin, s_begin + s_count); per-stream operands are addressed with the
+ *     ABSOLUTE stream index: row of stream s at ptr + s*ld (ld in elements).
+ *   - Pointers are device pointers unless stated; the CALLER owns every buffer.
+ *     Data operands (pools, stage, q, k_new, v_new, out) must be 16-byte
+ *     aligned and their row strides multiples of 16 bytes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     is complete when that stream is.  Calls on one state must be ordered on
+ *     one stream by the caller; distinct states are independent.
+ *   - Every call returns hkv_status and never aborts.  Host-detectable errors
+ *     return before anything is enqueued.  Invariant violations found on the
+ *     device set a sticky bit in *err, reported by hkv_check.
+ *   - Element type: bf16 (bit pattern in uint16) or fp32, for q, k, v and out.
+ *     Scores are fp32; arithmetic is fp32.
+ */
+#ifndef HKV_H
+#define HKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HKV_OK = 0,
+  HKV_E_INVAL = -1,        /* bad config or argument (null, misaligned, range) */
+  HKV_E_STATE = -2,        /* call out of order (decode before classification) */
+  HKV_E_CAPACITY = -3,     /* device found a stream over its capacity          */
+  HKV_E_HIP = -4,          /* HIP runtime error (launch, copy, sync)            */
+  HKV_E_UNSUPPORTED = -5   /* valid but not implemented (e.g. head_dim 96)     */
+} hkv_status;
+
+typedef enum { HKV_DT_BF16 = 0, HKV_DT_F32 = 1 } hkv_dtype;
+typedef enum { HKV_LOCAL = 0, HKV_GLOBAL = 1, HKV_FULL = 2 } hkv_label;
+
+/* Device error bits in *err. */
+#define HKV_ERRBIT_CAPACITY 1   /* append into a full Global/FULL stream          */
+#define HKV_ERRBIT_LAYOUT   2   /* count/label/budget inconsistent                */
+#define HKV_ERRBIT_SELECT   4   /* fewer eviction candidates than evictions       */
+
+typedef struct {
+  int32_t layers, batch, heads, head_dim;   /* head_dim in {64, 128}            */
+  int32_t dtype;                            /* hkv_dtype                        */
+  int32_t final_len;                        /* N: prefix + generated tokens     */
+  int32_t prefill_len;                      /* P: cached length at classification */
+  int32_t local_window;                     /* w                                */
+  float   tau;                              /* accumulation threshold, (0, 1]   */
+  int32_t rho_num, rho_den;                 /* rho as an exact fraction         */
+  int32_t split_dist;                       /* D: near/far split distance       */
+  int32_t w_obs;                            /* W: scoring window (queries)      */
+  int32_t evict_m;                          /* M: evictions per event (== W, even) */
+  int32_t full_cache;                       /* 1: uncompressed baseline layout  */
+} hkv_config;
+
+/* Cache state: device buffers owned by the caller (sizes from the helpers). */
+typedef struct {
+  void    *k_pool, *v_pool;   /* [pool_slots, head_dim] element type           */
+  int32_t *pos;               /* [pool_slots] position held by each slot       */
+  float   *score;             /* [pool_slots] STE importance (Global streams)  */
+  int64_t *base;              /* [S] first pool slot of each stream            */
+  int32_t *cap;               /* [S] slots reserved                            */
+  int32_t *count;             /* [S] slots present                             */
+  int32_t *budget;            /* [S] w (Local), B_g (Global), N (full)         */
+  int32_t *n_tokens;          /* [S] classification count                      */
+  uint8_t *label;             /* [S] hkv_label                                 */
+  int32_t *err;               /* [1] sticky device error bits                  */
+  void    *workspace;         /* hkv_workspace_bytes() bytes, 256-B aligned    */
+  size_t   workspace_bytes;
+  int32_t  phase;             /* host side: 0 new, 1 classified                */
+} hkv_state;
+
+/* Pool slots a state needs: S*(floor(rho*N) + M), or S*N for full_cache.
+ * Label-independent, so the caller allocates before classification.  0 if the
+ * config is invalid. */
+size_t hkv_pool_slots(const hkv_config *cfg);
+
+/* Workspace bytes for the state (classification scores plus the spill area for
+ * Global streams too long for on-chip scratch).  0 if the config is invalid. */
+size_t hkv_workspace_bytes(const hkv_config *cfg);
+
+/* Pure host check of a configuration; no HIP call. */
+hkv_status hkv_validate(const hkv_config *cfg);
+
+/* Steps 1-2: classification and initial layout, once per generation.
+ *   k_stage, v_stage: prefilled cache, stream s row p at ptr + s*ld_stage + p*head_dim
+ *   q_obs: the W last prefill queries (positions P-W .. P-1), stream s row r at
+ *          q_obs + s*ld_qobs + r*head_dim
+ * Writes label, n_tokens, budget, cap, base, count, pos, score and the pools for
+ * all S streams; sets phase = 1.  With full_cache every stream is FULL (slot =
+ * position) and q_obs may be NULL. */
+hkv_status hkv_classify(const hkv_config *cfg, hkv_state *st,
+                        const void *k_stage, const void *v_stage, int64_t ld_stage,
+                        const void *q_obs, int64_t ld_qobs, void *stream);
+
+/* Append token t (P <= t < N) to every stream of the range: Local slot t mod w,
+ * Global/FULL slot `count` (score 0).  k_new/v_new: row of stream s at
+ * ptr + s*ld_kv. */
+hkv_status hkv_append(const hkv_config *cfg, hkv_state *st, int32_t t,
+                      const void *k_new, const void *v_new, int64_t ld_kv,
+                      int32_t s_begin, int32_t s_count, void *stream);
+
+/* Decode attention at step t over the slots present (the cache already holds
+ * token t).  out row of stream s at out + s*ld_o.  For Global streams the
+ * softmax probabilities are added to score (written instead of added at the
+ * first query of each scoring window). */
+hkv_status hkv_decode_attn(const hkv_config *cfg, hkv_state *st, int32_t t,
+                           const void *q, int64_t ld_q, void *out, int64_t ld_o,
+                           int32_t s_begin, int32_t s_count, void *stream);
+
+/* STE at step t for every Global stream of the range whose count reached
+ * budget + M: evict M, tail-fill, count = budget.  evicted_pos_log (optional,
+ * device, [S, M] int32): evicted positions in ascending slot order, or -1 for
+ * streams that did not evict. */
+hkv_status hkv_ste_evict(const hkv_config *cfg, hkv_state *st, int32_t t,
+                         int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
+                         void *stream);
+
+/* One decode step in a single launch: exactly hkv_append, then hkv_decode_attn,
+ * then hkv_ste_evict, with identical results (bit for bit). */
+hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
+                           const void *k_new, const void *v_new, int64_t ld_kv,
+                           const void *q, int64_t ld_q, void *out, int64_t ld_o,
+                           int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
+                           void *stream);
+
+/* Synchronises `stream`, reads *err and maps it: CAPACITY bit -> HKV_E_CAPACITY,
+ * other bits -> HKV_E_STATE, 0 -> HKV_OK.  Does not clear the word. */
+hkv_status hkv_check(const hkv_config *cfg, const hkv_state *st, void *stream);
+
+/* Static text for a status code. */
+const char *hkv_status_string(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *hkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HKV_H */

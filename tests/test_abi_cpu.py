@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point,
+and its host-side checks return the documented status codes before any device
+work (no compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_compression_hkv_amd as hk
+from hkv_inputs.configs import WORKLOADS, full_cache_of
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "hkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hkv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(hk.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    base = dict(layers=2, batch=2, heads=4, head_dim=64, dtype="bf16", final_len=200,
+                prefill_len=40, local_window=16, tau=0.9, rho=(1, 4), split_dist=24)
+    base.update(kw)
+    return hk.make_config(**base)
+
+
+def test_validate_workloads_and_sizes():
+    for w in WORKLOADS.values():
+        c = hk.config_from_workload(w)
+        assert hk.hkv_validate(c) == hk.OK, (w.name, hk.hkv_last_error())
+        A = w.N * w.rho[0] // w.rho[1]
+        assert hk.hkv_pool_slots(c) == w.S * (A + w.evict_m)
+        f = hk.config_from_workload(full_cache_of(w))
+        assert hk.hkv_pool_slots(f) == w.S * w.N
+        assert hk.hkv_workspace_bytes(c) >= w.S * w.P * 4 + hk.hkv_pool_slots(c) * 12
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), hk.E_UNSUPPORTED),
+    (dict(head_dim=0), hk.E_UNSUPPORTED),
+    (dict(layers=0), hk.E_INVAL),
+    (dict(dtype="f16"), hk.OK),            # any non-bf16 string maps to f32
+    (dict(prefill_len=4), hk.E_INVAL),     # P < w_obs
+    (dict(final_len=40), hk.E_INVAL),      # N <= P
+    (dict(tau=0.0), hk.E_INVAL),
+    (dict(tau=1.5), hk.E_INVAL),
+    (dict(rho=(5, 4)), hk.E_INVAL),
+    (dict(rho=(1, 100)), hk.E_INVAL),      # floor(rho N) < w
+    (dict(evict_m=7, w_obs=7), hk.E_INVAL),
+    (dict(evict_m=6), hk.E_UNSUPPORTED),   # M != W
+    (dict(split_dist=4), hk.E_INVAL),
+    (dict(prefill_len=2000, final_len=3000), hk.E_UNSUPPORTED),
+    (dict(local_window=0), hk.E_INVAL),
+])
+def test_validate_rejects(kw, code):
+    c = _cfg(**kw)
+    assert hk.hkv_validate(c) == code, hk.hkv_last_error()
+    if code != hk.OK:
+        assert hk.hkv_pool_slots(c) == 0
+        assert hk.hkv_last_error()
+
+
+def _fake_state(cfg, phase=1):
+    """A state whose pointers are aligned but never dereferenced: every call
+    below fails its host checks before anything is enqueued."""
+    a = 1 << 20
+    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg), phase)
+    return st
+
+
+def test_entry_points_reject_before_launch():
+    cfg = _cfg()
+    st = _fake_state(cfg, phase=0)
+    buf = 1 << 21
+    with pytest.raises(hk.HkvError) as e:
+        hk.hkv_append(cfg, st, 40, buf, buf, 64, 0, 16)
+    assert e.value.status == hk.E_STATE
+    st.phase = 1
+    cases = [
+        (lambda: hk.hkv_append(cfg, st, 39, buf, buf, 64, 0, 16), hk.E_INVAL),       # t < P
+        (lambda: hk.hkv_append(cfg, st, 200, buf, buf, 64, 0, 16), hk.E_INVAL),      # t >= N
+        (lambda: hk.hkv_append(cfg, st, 40, buf + 2, buf, 64, 0, 16), hk.E_INVAL),   # align
+        (lambda: hk.hkv_append(cfg, st, 40, buf, buf, 63, 0, 16), hk.E_INVAL),       # stride
+        (lambda: hk.hkv_append(cfg, st, 40, None, buf, 64, 0, 16), hk.E_INVAL),
+        (lambda: hk.hkv_append(cfg, st, 40, buf, buf, 64, 10, 7), hk.E_INVAL),       # range
+        (lambda: hk.hkv_append(cfg, st, 40, buf, buf, 64, -1, 1), hk.E_INVAL),
+        (lambda: hk.hkv_decode_attn(cfg, st, 40, buf, 64, None, 64, 0, 16), hk.E_INVAL),
+        (lambda: hk.hkv_decode_attn(cfg, st, 40, buf, 64, buf, 32, 0, 16), hk.E_INVAL),
+        (lambda: hk.hkv_ste_evict(cfg, st, 40, buf + 2, 0, 16), hk.E_INVAL),
+        (lambda: hk.hkv_decode_step(cfg, st, 40, buf, buf, 64, buf, 64, buf, 64, None, 0, 17),
+         hk.E_INVAL),
+        (lambda: hk.hkv_classify(cfg, st, None, buf, 40 * 64, buf, 512), hk.E_INVAL),
+        (lambda: hk.hkv_classify(cfg, st, buf, buf, 10, buf, 512), hk.E_INVAL),
+        (lambda: hk.hkv_classify(cfg, st, buf, buf, 40 * 64, buf, 64), hk.E_INVAL),
+    ]
+    for i, (fn, code) in enumerate(cases):
+        with pytest.raises(hk.HkvError) as e:
+            fn()
+        assert e.value.status == code, (i, hk.hkv_last_error())
+    bad = hk.hkv_state(*([0] * 12), 0, 1)
+    with pytest.raises(hk.HkvError) as e:
+        hk.hkv_append(cfg, bad, 40, buf, buf, 64, 0, 16)
+    assert e.value.status == hk.E_INVAL
+    small_ws = _fake_state(cfg)
+    small_ws.workspace_bytes = 16
+    with pytest.raises(hk.HkvError) as e:
+        hk.hkv_append(cfg, small_ws, 40, buf, buf, 64, 0, 16)
+    assert e.value.status == hk.E_INVAL
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert hk.hkv_status_string(code)
+    assert hk.hkv_status_string(-99) == "unknown status"

@@ -1,0 +1,194 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle, on
+small workloads the oracle replays in full: several tiles, ragged tails, both
+element types, both head sizes and the method's degenerate cases."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():           # collected on CPU machines, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_compression_hkv_amd as hk
+import oracle.hkv_oracle as O
+from hkv_inputs import gen
+from hkv_inputs.configs import TINY
+from hkv_inputs.gpu import bits_of, device_inputs
+from tests._fixtures import small_config
+from tests._parity import gpu_generation, group_streams, oracle_check_group
+
+CASES = {
+    # initial STE (P > B_g), bf16, head_dim 64, 6 heads x 2 layers x 2 sequences
+    "bf16_d64_init_ste": small_config(layers=2, batch=2),
+    # no initial STE: Global heads grow from P to their budget first
+    "bf16_d128_growing": small_config(head_dim=128, rho=(1, 2), prefill_image=30),
+    "f32_d64": small_config(dtype="f32", heads=5),
+    "f32_d128": small_config(dtype="f32", head_dim=128, heads=3, rho=(1, 6), split_dist=40),
+    # near subset with one candidate: the far subset supplies the rest
+    "shortfall_near": small_config(split_dist=9),
+    # far subset empty: every eviction comes from the near subset
+    "far_empty": small_config(split_dist=400),
+    # rho = 1: Global heads never evict and equal full attention
+    "rho_one": small_config(rho=(1, 1), image_tokens=90),
+    # wide window: most heads Local
+    "wide_window": small_config(local_window=44, p_local=1.0),
+    # uncompressed baseline layout
+    "full_cache": small_config(full_cache=True, image_tokens=120),
+    # odd sizes everywhere
+    "ragged": small_config(heads=7, prefix=5, image_tokens=143, prefill_image=37,
+                           local_window=13, split_dist=21, rho=(2, 7)),
+    # Global streams longer than the on-chip scratch (spill to the workspace)
+    "long_global": small_config(heads=2, prefix=0, image_tokens=1500, prefill_image=64,
+                                rho=(3, 4), split_dist=300, p_local=0.0),
+}
+
+
+def _all_groups(w):
+    return [(l, b) for l in range(w.layers) for b in range(w.batch)]
+
+
+@pytest.mark.parametrize("name", ["tiny"] + sorted(CASES))
+def test_parity_small(name):
+    w = TINY if name == "tiny" else CASES[name]
+    print(f"[gpu] parity {name}: S={w.S} N={w.N} P={w.P} d={w.head_dim} {w.dtype}", flush=True)
+    groups = _all_groups(w)
+    g = gpu_generation(w, 0, group_streams(w, groups))
+    rep = None
+    for (l, b) in groups:
+        rep = oracle_check_group(w, 0, l, b, g, rep=rep)
+    print(f"  outputs {rep.outputs_checked} events {rep.events_checked} "
+          f"max err {rep.max_out_err:.3g} flags {rep.flagged_counts}/{rep.flagged_labels}/"
+          f"{rep.flagged_evictions}", flush=True)
+    assert not rep.failures, rep.failures[:8]
+    if name not in ("rho_one", "full_cache", "wide_window"):
+        assert rep.events_checked > 0
+
+
+def test_generator_twin_bits():
+    for w in (TINY, small_config(layers=2, batch=2), small_config(head_dim=128, dtype="f32")):
+        print(f"[gpu] generator twin {w.name} {w.dtype} d={w.head_dim}", flush=True)
+        K, V, Q = device_inputs(w, 3)
+        for (l, b) in _all_groups(w)[:3]:
+            kb, vb, qb = gen.group_inputs(w, 3, l, b)
+            s0 = w.stream(l, b, 0)
+            sl = slice(s0, s0 + w.heads)
+            assert np.array_equal(bits_of(K[sl]), kb)
+            assert np.array_equal(bits_of(V[sl]), vb)
+            assert np.array_equal(bits_of(Q[sl]), qb)
+
+
+def test_fused_equals_separate_calls():
+    """hkv_decode_step gives bit-identical results to append + attn + evict."""
+    w = small_config(layers=2, batch=2, heads=8)
+    print("[gpu] fused vs separate", flush=True)
+    inputs = device_inputs(w, 1)
+    streams = list(range(w.S))
+    a = gpu_generation(w, 1, streams, mode="fused", inputs=inputs)
+    b = gpu_generation(w, 1, streams, mode="split", inputs=inputs)
+    assert np.array_equal(a.outs, b.outs)
+    assert np.array_equal(a.logs, b.logs)
+    assert a.tables_final == b.tables_final
+    for x, y in zip(a.scores_final, b.scores_final):
+        assert np.array_equal(x, y)
+
+
+def test_determinism():
+    w = small_config(layers=1, batch=3, heads=6, head_dim=128)
+    print("[gpu] determinism", flush=True)
+    inputs = device_inputs(w, 2)
+    streams = list(range(w.S))
+    a = gpu_generation(w, 2, streams, inputs=inputs)
+    b = gpu_generation(w, 2, streams, inputs=inputs)
+    assert np.array_equal(a.outs, b.outs) and np.array_equal(a.logs, b.logs)
+    assert a.tables_final == b.tables_final
+
+
+def _events_of(w, seed=0):
+    K, V, Q = (gen.decode(x, w.dtype) for x in gen.group_inputs(w, seed, 0, 0))
+    return O.run_group(w, K, V, Q), K, V
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_evict_given_identical_scores(dtype, d):
+    """Load the oracle's pre-eviction state (layout and fp32-rounded scores) into
+    a GPU state and run hkv_ste_evict alone: the evicted set and the layout after
+    tail fill must equal the oracle's selection on the same fp32 scores, bit for bit."""
+    w = small_config(dtype=dtype, head_dim=d, heads=4, p_local=0.0, split_dist=20)
+    print(f"[gpu] evict given scores {dtype} d={d}", flush=True)
+    rec, K, V = _events_of(w)
+    events = rec.events[:12] + rec.events[-12:]
+    assert events
+    cfg = hk.config_from_workload(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for ev in events:
+        cache = hk.HkvCache(cfg)
+        s = ev.head
+        c = len(ev.slot_pos)
+        base = 0                        # only stream s is launched
+        assert c <= cache.slots
+        pos = np.array(ev.slot_pos, dtype=np.int32)
+        sc32 = np.array(ev.slot_score, dtype=np.float32)
+        cache.base[s] = base
+        cache.cap[s] = c
+        cache.count[s] = c
+        cache.budget[s] = ev.budget
+        cache.label[:] = hk.LOCAL
+        cache.label[s] = hk.GLOBAL
+        cache.pos[base:base + c] = torch.from_numpy(pos).cuda()
+        cache.score[base:base + c] = torch.from_numpy(sc32).cuda()
+        cache.k_pool[base:base + c] = torch.from_numpy(K[s][pos]).to(dt).cuda()
+        cache.v_pool[base:base + c] = torch.from_numpy(V[s][pos]).to(dt).cuda()
+        cache.state.phase = 1
+        log = torch.full((w.S, w.evict_m), -7, dtype=torch.int32, device="cuda")
+        hk.hkv_ste_evict(cfg, cache.state, ev.t, log, s, 1)
+        hk.hkv_check(cfg, cache.state)
+        own = O.ste_select(ev.slot_pos, sc32.astype(np.float64), ev.t, w.w_obs, w.split_dist,
+                           w.evict_m)
+        want_pos, _ = O.tail_fill(ev.slot_pos, list(sc32), own, ev.budget)
+        got_log = log[s].cpu().numpy()
+        assert sorted(got_log.tolist()) == sorted(ev.slot_pos[j] for j in own)
+        assert int(cache.count[s]) == ev.budget
+        got_pos = cache.pos[base:base + ev.budget].cpu().numpy().tolist()
+        assert got_pos == want_pos
+        got_k = cache.k_pool[base:base + ev.budget].float().cpu().numpy()
+        assert np.array_equal(got_k, K[s][want_pos].astype(np.float32)
+                              if dtype == "f32" else
+                              torch.from_numpy(K[s][want_pos]).to(dt).float().numpy())
+
+
+def test_capacity_error_reported():
+    """A Global stream already at capacity: append sets the device error word,
+    the kernel exits normally, hkv_check reports HKV_E_CAPACITY."""
+    w = small_config(p_local=0.0)
+    print("[gpu] capacity error", flush=True)
+    K, V, Q = device_inputs(w, 0)
+    cfg = hk.config_from_workload(w)
+    cache = hk.HkvCache(cfg)
+    hk.hkv_classify(cfg, cache.state, K, V, w.N * w.head_dim, Q, w.q_rows * w.head_dim)
+    hk.hkv_check(cfg, cache.state)
+    g = int(torch.nonzero(cache.label == hk.GLOBAL)[0])
+    cache.count[g] = cache.cap[g]
+    t = w.P
+    d = w.head_dim
+    hk.hkv_append(cfg, cache.state, t, K.data_ptr() + t * d * 2, V.data_ptr() + t * d * 2,
+                  w.N * d, 0, w.S)
+    with pytest.raises(hk.HkvError) as ei:
+        hk.hkv_check(cfg, cache.state)
+    assert ei.value.status == hk.E_CAPACITY
+
+
+def test_empty_range_and_phase():
+    w = small_config()
+    cfg = hk.config_from_workload(w)
+    cache = hk.HkvCache(cfg)
+    buf = torch.zeros((w.S, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(hk.HkvError) as ei:
+        hk.hkv_append(cfg, cache.state, w.P, buf, buf, w.head_dim, 0, w.S)
+    assert ei.value.status == hk.E_STATE
+    cache.state.phase = 1
+    assert hk.hkv_decode_attn(cfg, cache.state, w.P, buf, w.head_dim, buf, w.head_dim, 3, 0) == 0
+    with pytest.raises(hk.HkvError):
+        hk.hkv_decode_attn(cfg, cache.state, w.P, buf, w.head_dim, buf, w.head_dim, 3, w.S)
