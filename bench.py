@@ -1,0 +1,289 @@
+"""Benchmark of the HeadKV decode-time path on one MI355X.
+
+One benchmark step = one pass of the whole path over one batch: classification
+and initial layout (hkv_classify), then every decode step t = P .. N-1 as one
+fused launch (hkv_decode_step: append + attention with the eviction-score
+side-output + Stratified Token Eviction) over all layers x sequences x heads
+(layer-folded launch).  Inputs are synthetic, seeded, generated on the device
+before timing and resident in HBM.
+
+Default workload: LlamaGen-XL-shaped, bf16, 36 layers x 16 sequences x 20 heads,
+head_dim 64, N = 696, P = 184, rho = 1/6 (512 decode steps).
+
+Prints ONE JSON line.  value = generated tokens per second = batch * decode
+steps / step time.  The roofline block is for the dominant kernel (the fused
+decode step): algorithmic bytes per launch / mean launch time from HIP events
+recorded around every launch inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "compressed decode-attn tokens/s at rho=1/6; achieved HBM GB/s as % of peak"
+KERNEL_SOURCES = ("kv_cache_compression_hkv_amd/csrc/hkv_kernels.hip",
+                  "kv_cache_compression_hkv_amd/csrc/hkv_device.h")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hkv_decode_step_llamagen_xl_counters.json")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- bytes model
+def step_bytes(labels, budgets, w):
+    """Algorithmic bytes of every fused decode launch of one generation.
+
+    Per stream and step, with c the slots present after the append and
+    e the element size:  K and V rows 2*d*e*c, q in and o out 2*d*e, append
+    write 2*d*e + 4 (row and position); Global streams add the score
+    read-modify-write 8*c - 4 and, on an eviction step, the position reads 4*c
+    plus M moved slots (read + write of the K and V rows, position and score
+    writes).  Per-stream metadata (label, count, base, budget, cap) is 25 bytes.
+    """
+    import numpy as np
+    d, e, M, P, T = w.head_dim, w.elem_bytes, w.evict_m, w.P, w.steps
+    row = d * e
+    out = np.zeros(T)
+    glob = {}
+    for lab, B in zip(labels.tolist(), budgets.tolist()):
+        if lab == 2:                       # full cache
+            c = np.arange(P + 1, P + T + 1)
+            out += 2 * row * c + 2 * row + 2 * row + 4 + 25
+            continue
+        if lab == 0:                       # local ring
+            c = np.minimum(np.arange(P + 1, P + T + 1), w.local_window)
+            out += 2 * row * c + 2 * row + 2 * row + 4 + 25
+            continue
+        glob[B] = glob.get(B, 0) + 1
+    for B, n in glob.items():
+        cnt = min(P, B)
+        traj = np.zeros(T)
+        for i in range(T):
+            c = cnt + 1
+            b = 2 * row * c + 2 * row + 2 * row + 4 + 25 + 8 * c - 4
+            if c == B + M:
+                b += 4 * c + M * (4 * row + 8)
+                cnt = B
+            else:
+                cnt = c
+            traj[i] = b
+        out += n * traj
+    return out
+
+
+# ---------------------------------------------------------------- CPU baseline
+def _oracle_worker(args):
+    """Runs the oracle on a list of (layer, sequence) groups; times run_group only."""
+    name, groups, seed = args
+    from hkv_inputs.configs import WORKLOADS
+    from hkv_inputs import gen
+    import oracle.hkv_oracle as O
+    w = WORKLOADS[name]
+    data = []
+    for (l, b) in groups:
+        kb, vb, qb = gen.group_inputs(w, seed, l, b)
+        data.append((gen.decode(kb, w.dtype), gen.decode(vb, w.dtype), gen.decode(qb, w.dtype)))
+    t0 = time.perf_counter()
+    for K, V, Q in data:
+        O.run_group(w, K, V, Q)
+    return time.perf_counter() - t0, len(groups)
+
+
+def cpu_baseline(w, seed: int, groups_per_core: int = 2):
+    import multiprocessing as mp
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    groups = [(l % w.layers, (l // w.layers) % w.batch) for l in range(cores * groups_per_core)]
+    chunks = [(w.name, groups[i::cores], seed) for i in range(cores)]
+    ctx = mp.get_context("spawn")
+    env = dict(OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        with ctx.Pool(cores) as pool:
+            res = pool.map(_oracle_worker, chunks)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    wall = max(r[0] for r in res)
+    n_groups = sum(r[1] for r in res)
+    tokens = n_groups * w.steps / w.layers     # a token = one sequence through all layers
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_groups} (layer, sequence) groups of {w.name}, every decode step, "
+                      f"numpy fp64, one process per core, {wall:.1f} s wall"}
+
+
+# ---------------------------------------------------------------- GPU run
+class Generation:
+    def __init__(self, w, inputs, hk):
+        import torch
+        self.w, self.hk = w, hk
+        self.K, self.V, self.Q = inputs
+        self.cfg = hk.config_from_workload(w)
+        self.cache = hk.HkvCache(self.cfg)
+        self.out = torch.empty((w.S, w.head_dim), dtype=self.K.dtype, device=self.K.device)
+        d, eb = w.head_dim, w.elem_bytes
+        self.kp = [self.K.data_ptr() + t * d * eb for t in range(w.N)]
+        self.vp = [self.V.data_ptr() + t * d * eb for t in range(w.N)]
+        self.qp = [self.Q.data_ptr() + (t - (w.P - w.w_obs)) * d * eb for t in range(w.N)]
+
+    def run(self, stream, events=None):
+        w, hk, st = self.w, self.hk, self.cache.state
+        d = w.head_dim
+        hk.hkv_classify(self.cfg, st, self.K, self.V, w.N * d, self.Q, w.q_rows * d, stream)
+        for i, t in enumerate(range(w.P, w.N)):
+            if events is not None:
+                events[i][0].record(stream)
+            hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, self.qp[t],
+                               w.q_rows * d, self.out, d, None, 0, w.S, stream)
+            if events is not None:
+                events[i][1].record(stream)
+
+
+def time_generations(gen_obj, steps, warmup, with_events=True):
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        gen_obj.run(stream)
+    torch.cuda.synchronize()
+    T = gen_obj.w.steps
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(T)] for _ in range(steps)] if with_events else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        gen_obj.run(stream, evs[k] if evs else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = None
+    if evs:
+        per = [[a.elapsed_time(b) for a, b in ev] for ev in evs]
+        import numpy as np
+        kernel_ms = np.array(per)                  # [steps, T]
+    hk = gen_obj.hk
+    hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
+    return wall / steps * 1e3, kernel_ms
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the HBM counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llamagen_xl_rho1_6")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-cache", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode path is per-stream independent "
+              "and this build runs on a single MI355X; use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import kv_cache_compression_hkv_amd as hk
+    from hkv_inputs.configs import WORKLOADS, full_cache_of
+    from hkv_inputs.gpu import device_inputs
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    inputs = device_inputs(w, args.seed)
+
+    comp = Generation(w, inputs, hk)
+    ms, kern = time_generations(comp, args.steps, args.warmup)
+    labels = comp.cache.label.cpu().numpy()
+    budgets = comp.cache.budget.cpu().numpy()
+    alg = step_bytes(labels, budgets, w)                     # [T]
+    kern_mean_s = float(kern.mean()) * 1e-3
+    achieved = float(alg.mean()) / kern_mean_s / 1e9         # GB/s
+    tokens = w.batch * w.steps
+    value = tokens / (ms * 1e-3)
+
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            cnt = json.load(f)
+        if cnt.get("kernel_hash") == kernel_hash() and cnt.get("workload") == w.name:
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "heads": w.heads,
+                   "head_dim": w.head_dim, "final_len": w.N, "prefill_len": w.P,
+                   "rho": f"{w.rho[0]}/{w.rho[1]}", "decode_steps": w.steps,
+                   "launch": "layer-folded, 1 fused launch per decode step",
+                   "global_batch": w.batch, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_step (fused append + attention + STE)",
+                     "mean_launch_us": round(kern_mean_s * 1e6, 3),
+                     "alg_bytes_per_launch": round(float(alg.mean()), 1)},
+        "labels": {"local": int((labels == 0).sum()), "global": int((labels == 1).sum())},
+    }
+    if not args.no_full_cache:
+        wf = full_cache_of(w)
+        full = Generation(wf, inputs, hk)
+        del comp
+        torch.cuda.empty_cache()
+        ms_f, kern_f = time_generations(full, max(2, args.steps // 2), 1)
+        lab_f = full.cache.label.cpu().numpy()
+        alg_f = step_bytes(lab_f, full.cache.budget.cpu().numpy(), wf)
+        kf = float(kern_f.mean()) * 1e-3
+        res["full_cache"] = {"value": round(tokens / (ms_f * 1e-3), 1), "ms_per_step": round(ms_f, 4),
+                             "mean_launch_us": round(kf * 1e6, 3),
+                             "achieved_GBs": round(float(alg_f.mean()) / kf / 1e9, 1),
+                             "speedup_step": round(ms_f / ms, 3),
+                             "speedup_kernel": round(kf / kern_mean_s, 3)}
+        del full
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

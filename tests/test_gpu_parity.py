@@ -24,9 +24,10 @@ CASES = {
     # initial STE (P > B_g), bf16, head_dim 64, 6 heads x 2 layers x 2 sequences
     "bf16_d64_init_ste": small_config(layers=2, batch=2),
     # no initial STE: Global heads grow from P to their budget first
-    "bf16_d128_growing": small_config(head_dim=128, rho=(1, 2), prefill_image=30),
+    "bf16_d128_growing": small_config(head_dim=128, rho=(1, 2), prefill_image=30, p_local=0.0),
     "f32_d64": small_config(dtype="f32", heads=5),
-    "f32_d128": small_config(dtype="f32", head_dim=128, heads=3, rho=(1, 6), split_dist=40),
+    "f32_d128": small_config(dtype="f32", head_dim=128, heads=3, rho=(1, 6), split_dist=40,
+                            p_local=0.0),
     # near subset with one candidate: the far subset supplies the rest
     "shortfall_near": small_config(split_dist=9),
     # far subset empty: every eviction comes from the near subset
