@@ -262,6 +262,8 @@ def main():
                      "traffic": traffic,
                      "kernel": "k_step (fused append + attention + STE)",
                      "mean_launch_us": round(kern_mean_s * 1e6, 3),
+                     "median_launch_us": round(float(np.median(kern)) * 1e3, 3),
+                     "max_launch_us": round(float(kern.mean(axis=0).max()) * 1e3, 3),
                      "alg_bytes_per_launch": round(float(alg.mean()), 1)},
         "labels": {"local": int((labels == 0).sum()), "global": int((labels == 1).sum())},
     }

@@ -91,7 +91,8 @@ typedef struct {
   int32_t full_cache;                       /* 1: uncompressed baseline layout  */
 } hkv_config;
 
-/* Cache state: device buffers owned by the caller (sizes from the helpers). */
+/* Cache state: device buffers owned by the caller (sizes from the helpers).
+ * Index buffers must be aligned to their element size (label: 4 bytes). */
 typedef struct {
   void    *k_pool, *v_pool;   /* [pool_slots, head_dim] element type           */
   int32_t *pos;               /* [pool_slots] position held by each slot       */
@@ -101,7 +102,7 @@ typedef struct {
   int32_t *count;             /* [S] slots present                             */
   int32_t *budget;            /* [S] w (Local), B_g (Global), N (full)         */
   int32_t *n_tokens;          /* [S] classification count                      */
-  uint8_t *label;             /* [S] hkv_label                                 */
+  uint8_t *label;             /* [S] hkv_label (4-byte aligned)                */
   int32_t *err;               /* [1] sticky device error bits                  */
   void    *workspace;         /* hkv_workspace_bytes() bytes, 256-B aligned    */
   size_t   workspace_bytes;

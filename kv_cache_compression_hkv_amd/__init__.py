@@ -26,7 +26,8 @@ __all__ = [
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhkv.so")
+# HKV_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("HKV_LIBRARY") or os.path.join(HERE, "libhkv.so")
 
 OK, E_INVAL, E_STATE, E_CAPACITY, E_HIP, E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 DT_BF16, DT_F32 = 0, 1

@@ -82,6 +82,12 @@ __device__ inline float cross_group_sum(float x) {
 }
 
 __device__ inline float wave_max(float x) { return cross_group_max<1>(x); }
+
+__device__ inline int wave_sum_int(int x) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
 __device__ inline float wave_sum(float x) { return cross_group_sum<1>(x); }
 
 // Inclusive prefix sum over the wave (Hillis-Steele).

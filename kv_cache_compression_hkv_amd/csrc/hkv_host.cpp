@@ -90,7 +90,9 @@ hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st) {
   if (!aligned16(st->k_pool) || !aligned16(st->v_pool))
     return fail(HKV_E_INVAL, "k_pool/v_pool must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(st->base) & 7u) || (reinterpret_cast<uintptr_t>(st->pos) & 3u) ||
-      (reinterpret_cast<uintptr_t>(st->score) & 3u))
+      (reinterpret_cast<uintptr_t>(st->score) & 3u) || (reinterpret_cast<uintptr_t>(st->label) & 3u) ||
+      (reinterpret_cast<uintptr_t>(st->count) & 3u) || (reinterpret_cast<uintptr_t>(st->cap) & 3u) ||
+      (reinterpret_cast<uintptr_t>(st->budget) & 3u) || (reinterpret_cast<uintptr_t>(st->n_tokens) & 3u))
     return fail(HKV_E_INVAL, "state index buffers misaligned");
   Derived d;
   hkv_status s = derive(c, &d);

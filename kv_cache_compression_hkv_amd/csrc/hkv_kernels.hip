@@ -27,7 +27,21 @@
 namespace hkv {
 namespace dev {
 
-constexpr int kNW = 4;                 // waves per workgroup
+// Tuning knobs (compile-time): waves per workgroup, row fragments in flight per
+// lane, prefetched score slots per thread, minimum waves per SIMD.
+#ifndef HKV_NW
+#define HKV_NW 4
+#endif
+#ifndef HKV_U
+#define HKV_U 2
+#endif
+#ifndef HKV_KPT
+#define HKV_KPT 1
+#endif
+#ifndef HKV_WPE
+#define HKV_WPE 1
+#endif
+constexpr int kNW = HKV_NW;            // waves per workgroup
 constexpr int kNT = kNW * kWave;
 
 struct StepArgs {
@@ -42,12 +56,8 @@ struct StepArgs {
   int* err;
   float* ws_logits; uint64_t* ws_keys;
   int s_begin, t, w, W, M, D;
+  int S;                               // streams in the state (label array length)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
-};
-
-struct StepMeta {
-  long long base;
-  int lab, c, B, slot_new, ok, write_mode, due;
 };
 
 struct CombineShared {
@@ -56,77 +66,89 @@ struct CombineShared {
   float o[kNW][128];
 };
 
-// ------------------------------------------------------------------ k_step
+struct EvictShared {
+  int cnt[2];
+  int nh, nm, ne;
+  int holes[kMaxEvict], movers[kMaxEvict];
+  int mover_rank[kMaxEvict];           // tail slot B + r -> mover index, or -1
+};
+
+// Eviction key with the subset in the top bits: (subset << 62) | (score bits <<
+// 31) | position.  Scores are non-negative (sign bit clear) and positions are
+// below 2**31, so inside one subset keys order by (score, position) and the
+// subsets occupy disjoint key ranges.  Subset 2 = protected (not a candidate).
+__device__ inline uint64_t make_skey(int sub, float score, int pos) {
+  return (uint64_t(sub) << 62) | (uint64_t(__float_as_uint(score)) << 31) | uint32_t(pos);
+}
+__device__ inline int skey_sub(uint64_t k) { return int(k >> 62); }
+__device__ inline int skey_pos(uint64_t k) { return int(uint32_t(k) & 0x7fffffffu); }
+__device__ inline float skey_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 31) & 0x7fffffffu); }
+
+// Source of fragment idx of the tail rows [B, B + M): row B + idx / (2G), K
+// (first G fragments of the row) or V, 16-byte piece idx % G; the token appended
+// in this launch is read from its source row.
+template <class T, int D, bool AP>
+__device__ inline const char* tail_src_impl(const StepArgs& a, int s, long long base,
+                                            int slot_new, int B, int idx) {
+  constexpr int VE = Frag<T>::N, G = D / VE, ES = sizeof(T);
+  const int row = B + idx / (2 * G);
+  const bool isv = (idx % (2 * G)) >= G;
+  const int sb = idx % G;
+  if (AP && row == slot_new)
+    return (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sb * VE) * ES;
+  return (isv ? a.v_pool : a.k_pool) + ((base + row) * D + sb * VE) * ES;
+}
+
+// Body of a decode step for one stream after its metadata is known.  `lg`,
+// `keys` and `evf` are per-slot scratch: on chip (LDS) for streams of at most
+// kLdsSlots slots, else in the workspace; instantiating both cases lets the
+// compiler address the on-chip case with LDS instructions.
+struct StepCtx {
+  long long base;
+  int s, lab, c, B, slot_new;
+  bool glob, write_mode, due;
+};
+
 template <class T, int D, bool AP, bool AT, bool EV>
-__global__ __launch_bounds__(kNT) void k_step(StepArgs a) {
+__device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, uint4 q_raw,
+                                          float* lg, uint64_t* keys, uint8_t* evf,
+                                          CombineShared& cs, EvictShared& es) {
   using F = Frag<T>;
   constexpr int VE = F::N;           // elements per 16-byte fragment
   constexpr int G = D / VE;          // lanes per row
   constexpr int R = kWave / G;       // rows per wave instruction
-  constexpr int U = (32 / R) < 8 ? (32 / R) : 8;   // row fragments in flight per lane
+  constexpr int U = HKV_U;           // row fragments in flight per lane
   constexpr int ES = sizeof(T);
-
-  __shared__ StepMeta sm;
-  __shared__ CombineShared cs;
-  __shared__ SelectShared ss;
-  __shared__ float lds_lg[AT ? kLdsSlots : 1];
-  __shared__ uint64_t lds_key[EV ? kLdsSlots : 1];
-  __shared__ int holes[kMaxEvict], movers[kMaxEvict];
-  __shared__ int nmove;
-
+  constexpr int KPT = HKV_KPT;       // prefetched score slots per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = a.s_begin + blockIdx.x;
+  const int g = lane / G, sub = lane % G;
+  const long long base = x.base;
+  const int s = x.s, c = x.c, B = x.B, slot_new = x.slot_new;
+  const bool glob = x.glob, write_mode = x.write_mode, due = x.due;
+  auto tail_src = [](const StepArgs& aa, int ss, long long bb, int sn, int BB, int idx) {
+    return tail_src_impl<T, D, AP>(aa, ss, bb, sn, BB, idx);
+  };
 
-  if (tid == 0) {
-    const int lab = a.label[s];
-    const int c0 = a.count[s];
-    const int capv = a.cap[s];
-    const int B = a.budget[s];
-    int c = c0, slot_new = -1, ok = 1;
-    if (AP) {
-      if (lab == HKV_LOCAL) {
-        slot_new = a.t % a.w;
-        c = c0 + 1 < a.w ? c0 + 1 : a.w;
-      } else {
-        if (c0 >= capv) {
-          atomicOr(a.err, HKV_ERRBIT_CAPACITY);
-          ok = 0;
-        }
-        slot_new = c0;
-        c = c0 + 1;
-      }
-    }
-    if (ok && (c < 1 || c > capv || lab > HKV_FULL)) {
-      atomicOr(a.err, HKV_ERRBIT_LAYOUT);
-      ok = 0;
-    }
-    const bool glob = lab == HKV_GLOBAL;
-    sm.base = a.base[s];
-    sm.lab = lab;
-    sm.c = c;
-    sm.B = B;
-    sm.slot_new = slot_new;
-    sm.ok = ok;
-    sm.write_mode = glob && (c == B + a.M - a.W + 1);
-    sm.due = EV && glob && (c == B + a.M);
+  // prefetch the score window and, on an eviction step, the positions
+  float sc_old[KPT > 0 ? KPT : 1];
+  int pos_old[KPT > 0 ? KPT : 1];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int j = tid + k * kNT;
+    const bool fresh = AP && j == slot_new;
+    sc_old[k] = 0.f;
+    pos_old[k] = 0;
+    if (j < c && glob && !fresh && (due || (AT && !write_mode))) sc_old[k] = a.score[base + j];
+    if (j < c && due) pos_old[k] = fresh ? a.t : a.pos[base + j];
   }
-  __syncthreads();
-  const long long base = sm.base;
-  const int lab = sm.lab, c = sm.c, B = sm.B, slot_new = sm.slot_new;
-  const bool glob = lab == HKV_GLOBAL;
-  if (!sm.ok) {
-    if (EV && a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
-    return;
-  }
-  const bool due = sm.due;
 
   // ---------------- append token t
   if (AP) {
     if (tid < 2 * G) {
       const bool isv = tid >= G;
-      const int sub = tid % G;
-      const char* src = (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sub * VE) * ES;
-      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * D + sub * VE) * ES;
+      const int sb = tid % G;
+      const char* src = (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sb * VE) * ES;
+      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * D + sb * VE) * ES;
       st16(dst, ld16(src));
     }
     if (tid == 0) {
@@ -136,14 +158,12 @@ __global__ __launch_bounds__(kNT) void k_step(StepArgs a) {
   }
 
   // ---------------- attention over slots [0, c)
-  float* lg = (glob && c <= kLdsSlots) ? lds_lg : a.ws_logits + base;
   float Mx = 0.f, inv_l = 0.f;
   if (AT) {
-    const int g = lane / G, sub = lane % G;
     float qv[VE];
     {
       float qf[VE];
-      F::to_f32(ld16(a.q + ((long long)s * a.ld_q + sub * VE) * ES), qf);
+      F::to_f32(q_raw, qf);
 #pragma unroll
       for (int i = 0; i < VE; ++i) qv[i] = qf[i] * a.scale_log2;
     }
@@ -242,92 +262,169 @@ __global__ __launch_bounds__(kNT) void k_step(StepArgs a) {
     }
   }
 
-  // ---------------- score side-output (Global streams)
-  uint64_t* keys = (c <= kLdsSlots) ? lds_key : a.ws_keys + base;
-  if (AT && glob) {
-    for (int j = tid; j < c; j += kNT) {
-      const float p = exp2f(lg[j] - Mx) * inv_l;
+  // ---------------- score side-output (Global streams) / eviction keys
+  if (!AT && due) __syncthreads();                     // counters zeroed
+  if (glob && (AT || due)) {
+    const int t = a.t, W = a.W, Dd = a.D;
+    int nn = 0, nf = 0;
+    auto handle = [&](int j, float old, int pos_j) {
       const bool fresh = AP && j == slot_new;
-      const float ns = (fresh || sm.write_mode) ? p : a.score[base + j] + p;
-      if (due)
-        keys[j] = make_key(ns, fresh ? a.t : a.pos[base + j]);
-      else
+      float ns = old;
+      if (AT) {
+        const float p = exp2f(lg[j] - Mx) * inv_l;
+        ns = (fresh || write_mode) ? p : old + p;
+      } else if (fresh) {
+        ns = 0.0f;
+      }
+      if (due) {
+        const int dist = t - pos_j;
+        const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
+        nn += sb == 0;
+        nf += sb == 1;
+        keys[j] = make_skey(sb, ns, pos_j);
+      } else {
         a.score[base + j] = ns;
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = tid + k * kNT;
+      if (j < c) handle(j, sc_old[k], pos_old[k]);
     }
-  } else if (EV && due) {
-    for (int j = tid; j < c; j += kNT) {
+    for (int j = tid + KPT * kNT; j < c; j += kNT) {
       const bool fresh = AP && j == slot_new;
-      keys[j] = make_key(fresh ? 0.0f : a.score[base + j], fresh ? a.t : a.pos[base + j]);
+      const float old = (!fresh && (due || !write_mode)) ? a.score[base + j] : 0.f;
+      handle(j, old, due ? (fresh ? a.t : a.pos[base + j]) : 0);
+    }
+    if (due) {
+      nn = wave_sum_int(nn);
+      nf = wave_sum_int(nf);
+      if (lane == 0) {
+        if (nn) atomicAdd(&es.cnt[0], nn);
+        if (nf) atomicAdd(&es.cnt[1], nf);
+      }
     }
   }
 
   // ---------------- Stratified Token Eviction (due Global streams)
   int c_final = c;
   if (EV && due) {
-    __syncthreads();
-    ste_quotas<kNT>(keys, c, a.t, a.W, a.D, a.M, ss);
-    if (!ss.ok) {
+    // Every mover lies in the tail [B, c) (c - B = M on an eviction step): fetch
+    // those rows now so the loads overlap the selection.  Fragment idx of the
+    // tail: row B + idx / (2G), K or V, 16-byte piece idx % G.
+    constexpr int MVF = 2;                             // fragments fetched per thread
+    const int n_frag = 2 * G * (c - B);
+    uint4 mv_frag[MVF];
+#pragma unroll
+    for (int f = 0; f < MVF; ++f) {
+      const int idx = tid + f * kNT;
+      mv_frag[f] = make_uint4(0, 0, 0, 0);
+      if (idx < n_frag) mv_frag[f] = ld16(tail_src(a, s, base, slot_new, B, idx));
+    }
+    __syncthreads();                                   // keys and subset sizes complete
+    // Quotas: floor(M/2) near, the rest far; a short subset gives all it has.
+    const int E = a.M;
+    const int nn = es.cnt[0], nf = es.cnt[1];
+    int qn = E / 2, qf = E - qn;
+    if (nn < qn) {
+      qn = nn;
+      qf = E - qn;
+    } else if (nf < qf) {
+      qf = nf;
+      qn = E - qf;
+    }
+    const bool sel_ok = qn <= nn && qf <= nf;
+    // Rank of each candidate inside its subset (keys of one subset form one
+    // key range); evicted iff rank < quota.
+    if (sel_ok) {
+      for (int j = tid; j < c; j += kNT) {
+        const uint64_t kj = keys[j];
+        const int sb = skey_sub(kj);
+        const uint64_t lo = uint64_t(sb & 1) << 62;
+        int r = 0;
+        int i = 0;
+        for (; i + 8 <= c; i += 8) {
+          uint64_t kk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) kk[u] = keys[i + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r += (kk[u] >= lo) & (kk[u] < kj);
+        }
+        for (; i < c; ++i) {
+          const uint64_t ki = keys[i];
+          r += (ki >= lo) & (ki < kj);
+        }
+        evf[j] = (sb < 2 && r < (sb == 0 ? qn : qf)) ? 1 : 0;
+      }
+    }
+    if (!sel_ok) {
       if (tid == 0) atomicOr(a.err, HKV_ERRBIT_SELECT);
+      if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
     } else {
-      ste_radix_select<kNT>(keys, c, a.t, a.W, a.D, ss);
+      __syncthreads();
       if (wave == 0) {
         int nh = 0, nm = 0, ne = 0;
         const uint64_t lt = lanemask_lt(lane);
         for (int j0 = 0; j0 < c; j0 += kWave) {
           const int j = j0 + lane;
           const bool in = j < c;
-          const uint64_t k = in ? keys[j] : 0ull;
-          const bool ev = in && is_evicted(k, a.t, a.W, a.D, ss);
+          const bool ev = in && evf[j];
           const bool hole = ev && j < B;
           const bool mover = in && !ev && j >= B;
           const uint64_t mh = __ballot(hole), mm = __ballot(mover), me = __ballot(ev);
           if (hole) {
             const int r = nh + __popcll(mh & lt);
-            if (r < kMaxEvict) holes[r] = j;
+            if (r < kMaxEvict) es.holes[r] = j;
           }
           if (mover) {
             const int r = nm + __popcll(mm & lt);
-            if (r < kMaxEvict) movers[r] = j;
+            if (r < kMaxEvict) es.movers[r] = j;
           }
+          if (j >= B && j < B + a.M) es.mover_rank[j - B] = mover ? nm + __popcll(mm & lt) : -1;
           if (ev && a.log) {
             const int r = ne + __popcll(me & lt);
-            if (r < a.M) a.log[(long long)s * a.M + r] = key_pos(k);
+            if (r < a.M) a.log[(long long)s * a.M + r] = skey_pos(keys[j]);
           }
           nh += __popcll(mh);
           nm += __popcll(mm);
           ne += __popcll(me);
         }
-        if (lane == 0) nmove = (nh == nm && ne == a.M && nh <= kMaxEvict) ? nh : -1;
-        if (a.log && lane + ne < a.M && lane < a.M) a.log[(long long)s * a.M + ne + lane] = -1;
+        if (lane == 0) {
+          es.nh = nh;
+          es.nm = nm;
+          es.ne = ne;
+        }
+        if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
       }
       __syncthreads();
-      const int nmv = nmove;
-      if (nmv < 0) {
+      const int nmv = es.nh;
+      if (es.nh != es.nm || es.ne != a.M || es.nh > kMaxEvict) {
         if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
       } else {
-        // K/V rows of the movers into the holes
-        for (int idx = tid; idx < nmv * 2 * G; idx += kNT) {
-          const int k = idx / (2 * G), r = idx % (2 * G);
-          const bool isv = r >= G;
-          const int sub = r % G;
-          const int from = movers[k], to = holes[k];
-          const char* src;
-          if (AP && from == slot_new)
-            src = (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sub * VE) * ES;
-          else
-            src = (isv ? a.v_pool : a.k_pool) + ((base + from) * D + sub * VE) * ES;
-          st16((isv ? a.v_pool : a.k_pool) + ((base + to) * D + sub * VE) * ES, ld16(src));
+        // K/V rows of the movers into the holes (tail fill), mostly from the
+        // fragments fetched before the selection
+        for (int idx = tid, f = 0; idx < n_frag; idx += kNT, ++f) {
+          const int k = es.mover_rank[idx / (2 * G)];
+          if (k < 0) continue;
+          uint4 v;
+          if (f < MVF) {
+#pragma unroll
+            for (int ff = 0; ff < MVF; ++ff)
+              if (ff == f) v = mv_frag[ff];
+          } else {
+            v = ld16(tail_src(a, s, base, slot_new, B, idx));
+          }
+          const bool isv = (idx % (2 * G)) >= G;
+          st16((isv ? a.v_pool : a.k_pool) + ((base + es.holes[k]) * D + (idx % G) * VE) * ES, v);
         }
         if (tid < nmv) {
-          const uint64_t mk = keys[movers[tid]];
-          a.pos[base + holes[tid]] = key_pos(mk);
-          a.score[base + holes[tid]] = key_score(mk);
+          const uint64_t mk = keys[es.movers[tid]];
+          a.pos[base + es.holes[tid]] = skey_pos(mk);
+          a.score[base + es.holes[tid]] = skey_score(mk);
         }
-        if (AT) {   // deferred score writes of the kept slots
-          for (int j = tid; j < B; j += kNT) {
-            const uint64_t k = keys[j];
-            if (!is_evicted(k, a.t, a.W, a.D, ss)) a.score[base + j] = key_score(k);
-          }
+        if (AT) {   // deferred score writes of the kept slots below the budget
+          for (int j = tid; j < B; j += kNT)
+            if (!evf[j]) a.score[base + j] = skey_score(keys[j]);
         }
         c_final = B;
       }
@@ -337,6 +434,92 @@ __global__ __launch_bounds__(kNT) void k_step(StepArgs a) {
   }
 
   if (tid == 0 && (AP || c_final != c)) a.count[s] = c_final;
+}
+
+// ------------------------------------------------------------------ k_step
+// One workgroup per stream.  Every thread reads the stream's metadata itself
+// (uniform loads, no barrier); the query, the score window and the positions
+// needed by an eviction are requested together with the first K/V rows.
+template <class T, int D, bool AP, bool AT, bool EV>
+__global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
+  using F = Frag<T>;
+  constexpr int VE = F::N;           // elements per 16-byte fragment
+  constexpr int G = D / VE;          // lanes per row
+  constexpr int R = kWave / G;       // rows per wave instruction
+  constexpr int U = HKV_U;           // row fragments in flight per lane
+  constexpr int ES = sizeof(T);
+  constexpr int KPT = HKV_KPT;       // prefetched score slots per thread
+
+  __shared__ CombineShared cs;
+  __shared__ EvictShared es;
+  __shared__ float lds_lg[AT ? kLdsSlots : 1];
+  __shared__ uint64_t lds_key[EV ? kLdsSlots : 1];
+  __shared__ uint8_t lds_evf[EV ? kLdsSlots : 1];
+  (void)R; (void)U; (void)KPT;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = a.s_begin + blockIdx.x;
+  const int g = lane / G, sub = lane % G;
+  if (EV && tid < 2) es.cnt[tid] = 0;
+
+  // query fragment first: its address does not depend on the stream metadata
+  uint4 q_raw = make_uint4(0, 0, 0, 0);
+  if (AT) q_raw = ld16(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
+
+  // the label byte through the scalar path (aligned 32-bit word), except in a
+  // last partial word
+  int lab;
+  if (4LL * ((s >> 2) + 1) <= a.S)
+    lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
+  else
+    lab = a.label[s];
+  const int c0 = a.count[s];
+  const int capv = a.cap[s];
+  const int B = a.budget[s];
+  const long long base = a.base[s];
+  const bool glob = lab == HKV_GLOBAL;
+  int c = c0, slot_new = -1;
+  bool ok = true;
+  if (AP) {
+    if (lab == HKV_LOCAL) {
+      slot_new = a.t % a.w;
+      c = c0 + 1 < a.w ? c0 + 1 : a.w;
+    } else {
+      slot_new = c0;
+      c = c0 + 1;
+      if (c0 >= capv) {
+        ok = false;
+        if (tid == 0) atomicOr(a.err, HKV_ERRBIT_CAPACITY);
+      }
+    }
+  }
+  if (ok && (c < 1 || c > capv || lab > HKV_FULL)) {
+    ok = false;
+    if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
+  }
+  if (!ok) {
+    if (EV && a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
+    return;
+  }
+  const bool write_mode = glob && (c == B + a.M - a.W + 1);
+  const bool due = EV && glob && (c == B + a.M);
+
+  StepCtx x;
+  x.base = base;
+  x.s = s;
+  x.lab = lab;
+  x.c = c;
+  x.B = B;
+  x.slot_new = slot_new;
+  x.glob = glob;
+  x.write_mode = write_mode;
+  x.due = due;
+  (void)lane; (void)wave; (void)g;
+  if (c <= kLdsSlots)
+    step_body<T, D, AP, AT, EV>(a, x, q_raw, lds_lg, lds_key, lds_evf, cs, es);
+  else
+    step_body<T, D, AP, AT, EV>(a, x, q_raw, a.ws_logits + base, a.ws_keys + base,
+                                reinterpret_cast<uint8_t*>(a.ws_logits + base), cs, es);
 }
 
 // ------------------------------------------------------------------ k_classify
@@ -616,6 +799,7 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.M = c->evict_m;
   a.D = c->split_dist;
   a.scale_log2 = scale_log2_of(c->head_dim);
+  a.S = int(d.S);
   return a;
 }
 
