@@ -47,26 +47,27 @@ def kernel_hash() -> str:
 def step_bytes(labels, budgets, w):
     """Algorithmic bytes of every fused decode launch of one generation.
 
-    Per stream and step, with c the slots present after the append and
-    e the element size:  K and V rows 2*d*e*c, q in and o out 2*d*e, append
-    write 2*d*e + 4 (row and position); Global streams add the score
-    read-modify-write 8*c - 4 and, on an eviction step, the position reads 4*c
-    plus M moved slots (read + write of the K and V rows, position and score
-    writes).  Per-stream metadata (label, count, base, budget, cap) is 25 bytes.
+    Per stream and step, with c the slots holding a token after the append and
+    e the element size: K and V rows 2*d*e*c, query in and output out 2*d*e,
+    append write 2*d*e + 8 (row, position, score reset for Global streams) and
+    33 bytes of per-stream metadata (label, extent, capacity, budget, base, free
+    count; extent written back).  A Global stream at an eviction step also reads
+    its W-query window ((W-1)*d*e beyond the current query) and the positions of
+    its c slots (4*c), and writes its free list, the freed positions and the free
+    count (8*M + 4).
     """
     import numpy as np
-    d, e, M, P, T = w.head_dim, w.elem_bytes, w.evict_m, w.P, w.steps
+    d, e, M, P, T, W = w.head_dim, w.elem_bytes, w.evict_m, w.P, w.steps, w.w_obs
     row = d * e
+    base_bytes = lambda c: 2 * row * c + 2 * row + 2 * row + 8 + 33
     out = np.zeros(T)
     glob = {}
     for lab, B in zip(labels.tolist(), budgets.tolist()):
         if lab == 2:                       # full cache
-            c = np.arange(P + 1, P + T + 1)
-            out += 2 * row * c + 2 * row + 2 * row + 4 + 25
+            out += base_bytes(np.arange(P + 1, P + T + 1))
             continue
         if lab == 0:                       # local ring
-            c = np.minimum(np.arange(P + 1, P + T + 1), w.local_window)
-            out += 2 * row * c + 2 * row + 2 * row + 4 + 25
+            out += base_bytes(np.minimum(np.arange(P + 1, P + T + 1), w.local_window))
             continue
         glob[B] = glob.get(B, 0) + 1
     for B, n in glob.items():
@@ -74,9 +75,9 @@ def step_bytes(labels, budgets, w):
         traj = np.zeros(T)
         for i in range(T):
             c = cnt + 1
-            b = 2 * row * c + 2 * row + 2 * row + 4 + 25 + 8 * c - 4
+            b = base_bytes(c)
             if c == B + M:
-                b += 4 * c + M * (4 * row + 8)
+                b += (W - 1) * row + 4 * c + 8 * M + 4
                 cnt = B
             else:
                 cnt = c
@@ -145,44 +146,45 @@ class Generation:
         d, eb = w.head_dim, w.elem_bytes
         self.kp = [self.K.data_ptr() + t * d * eb for t in range(w.N)]
         self.vp = [self.V.data_ptr() + t * d * eb for t in range(w.N)]
-        self.qp = [self.Q.data_ptr() + (t - (w.P - w.w_obs)) * d * eb for t in range(w.N)]
+        # window of the W newest queries (positions t-W+1 .. t) for step t
+        self.qw = [self.Q.data_ptr() + (t - w.w_obs + 1 - (w.P - w.w_obs)) * d * eb
+                   for t in range(w.N)]
 
     def run(self, stream, events=None):
+        """One generation; `events` = (start, end) recorded around the decode loop."""
         w, hk, st = self.w, self.hk, self.cache.state
         d = w.head_dim
         hk.hkv_classify(self.cfg, st, self.K, self.V, w.N * d, self.Q, w.q_rows * d, stream)
-        for i, t in enumerate(range(w.P, w.N)):
-            if events is not None:
-                events[i][0].record(stream)
-            hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, self.qp[t],
+        if events is not None:
+            events[0].record(stream)
+        for t in range(w.P, w.N):
+            hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, self.qw[t],
                                w.q_rows * d, self.out, d, None, 0, w.S, stream)
-            if events is not None:
-                events[i][1].record(stream)
+        if events is not None:
+            events[1].record(stream)
 
 
-def time_generations(gen_obj, steps, warmup, with_events=True):
+def time_generations(gen_obj, steps, warmup):
+    """Mean ms per generation over `steps` timed generations, and the mean
+    duration of one decode-step launch (HIP events bracketing each generation's
+    decode loop on the launch stream, divided by the launches; the short gaps
+    between consecutive launches are included)."""
+    import numpy as np
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         gen_obj.run(stream)
-    torch.cuda.synchronize()
-    T = gen_obj.w.steps
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(T)] for _ in range(steps)] if with_events else None
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        gen_obj.run(stream, evs[k] if evs else None)
+        gen_obj.run(stream, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = None
-    if evs:
-        per = [[a.elapsed_time(b) for a, b in ev] for ev in evs]
-        import numpy as np
-        kernel_ms = np.array(per)                  # [steps, T]
-    hk = gen_obj.hk
-    hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
-    return wall / steps * 1e3, kernel_ms
+    loop_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
+    return wall / steps * 1e3, loop_ms / gen_obj.w.steps
 
 
 def copy_calibration():
@@ -231,11 +233,11 @@ def main():
     inputs = device_inputs(w, args.seed)
 
     comp = Generation(w, inputs, hk)
-    ms, kern = time_generations(comp, args.steps, args.warmup)
+    ms, launch_ms = time_generations(comp, args.steps, args.warmup)
     labels = comp.cache.label.cpu().numpy()
     budgets = comp.cache.budget.cpu().numpy()
     alg = step_bytes(labels, budgets, w)                     # [T]
-    kern_mean_s = float(kern.mean()) * 1e-3
+    kern_mean_s = float(launch_ms.mean()) * 1e-3
     achieved = float(alg.mean()) / kern_mean_s / 1e9         # GB/s
     tokens = w.batch * w.steps
     value = tokens / (ms * 1e-3)
@@ -262,8 +264,6 @@ def main():
                      "traffic": traffic,
                      "kernel": "k_step (fused append + attention + STE)",
                      "mean_launch_us": round(kern_mean_s * 1e6, 3),
-                     "median_launch_us": round(float(np.median(kern)) * 1e3, 3),
-                     "max_launch_us": round(float(kern.mean(axis=0).max()) * 1e3, 3),
                      "alg_bytes_per_launch": round(float(alg.mean()), 1)},
         "labels": {"local": int((labels == 0).sum()), "global": int((labels == 1).sum())},
     }
@@ -272,10 +272,10 @@ def main():
         full = Generation(wf, inputs, hk)
         del comp
         torch.cuda.empty_cache()
-        ms_f, kern_f = time_generations(full, max(2, args.steps // 2), 1)
+        ms_f, launch_f = time_generations(full, max(2, args.steps // 2), 1)
         lab_f = full.cache.label.cpu().numpy()
         alg_f = step_bytes(lab_f, full.cache.budget.cpu().numpy(), wf)
-        kf = float(kern_f.mean()) * 1e-3
+        kf = float(launch_f.mean()) * 1e-3
         res["full_cache"] = {"value": round(tokens / (ms_f * 1e-3), 1), "ms_per_step": round(ms_f, 4),
                              "mean_launch_us": round(kf * 1e6, 3),
                              "achieved_GBs": round(float(alg_f.mean()) / kf / 1e9, 1),

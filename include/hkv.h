@@ -26,13 +26,15 @@
  *   - budget per (layer, sequence): A = floor(N*rho_num/rho_den), Local heads w
  *     slots, Global heads B_g = floor((H*A - n_L*w) / n_G), capacity B_g + M;
  *   - score of a slot = sum of the softmax probabilities it received from the
- *     last W queries (W = w_obs = M); the W newest tokens are not candidates;
+ *     last W queries (W = w_obs = M), evaluated at the eviction step as the
+ *     causal W x count probability tile; the W newest tokens are not candidates;
  *     near: W <= t-pos < D, far: t-pos >= D; quotas floor(E/2) near and the
  *     rest far, a short subset gives all it has; order (score, position);
- *   - layout: Local slot = pos mod w; Global slots compact, evicted slots below
- *     B_g refilled in ascending order by the surviving tail slots; at
- *     classification an over-long Global prefix is reduced by STE with the W
- *     last prefill queries, survivors in ascending position order.
+ *   - layout: Local slot = pos mod w; Global: an eviction frees the evicted
+ *     slots (position -1) without moving any row, and the next tokens fill the
+ *     freed slots in ascending order before the table grows; at classification
+ *     an over-long Global prefix is reduced by STE with the W last prefill
+ *     queries, survivors compacted in ascending position order.
  *
  * Conventions (every entry point):
  *   - Streams: s = (l*batch + b)*heads + h.  Calls on a stream range take
@@ -96,13 +98,15 @@ typedef struct {
 typedef struct {
   void    *k_pool, *v_pool;   /* [pool_slots, head_dim] element type           */
   int32_t *pos;               /* [pool_slots] position held by each slot       */
-  float   *score;             /* [pool_slots] STE importance (Global streams)  */
+  float   *score;             /* [pool_slots] STE scores at the last eviction  */
   int64_t *base;              /* [S] first pool slot of each stream            */
   int32_t *cap;               /* [S] slots reserved                            */
-  int32_t *count;             /* [S] slots present                             */
+  int32_t *count;             /* [S] slots in use, including freed ones        */
   int32_t *budget;            /* [S] w (Local), B_g (Global), N (full)         */
   int32_t *n_tokens;          /* [S] classification count                      */
   uint8_t *label;             /* [S] hkv_label (4-byte aligned)                */
+  int32_t *free_slots;        /* [S, M] slots freed by the last eviction       */
+  int32_t *n_free;            /* [S] of those, how many are still free         */
   int32_t *err;               /* [1] sticky device error bits                  */
   void    *workspace;         /* hkv_workspace_bytes() bytes, 256-B aligned    */
   size_t   workspace_bytes;
@@ -132,34 +136,42 @@ hkv_status hkv_classify(const hkv_config *cfg, hkv_state *st,
                         const void *k_stage, const void *v_stage, int64_t ld_stage,
                         const void *q_obs, int64_t ld_qobs, void *stream);
 
-/* Append token t (P <= t < N) to every stream of the range: Local slot t mod w,
- * Global/FULL slot `count` (score 0).  k_new/v_new: row of stream s at
- * ptr + s*ld_kv. */
+/* Append token t (P <= t < N) to every stream of the range: Local slot t mod w;
+ * Global: the lowest freed slot if any, else slot `count` (score 0); FULL slot
+ * `count`.  k_new/v_new: row of stream s at ptr + s*ld_kv. */
 hkv_status hkv_append(const hkv_config *cfg, hkv_state *st, int32_t t,
                       const void *k_new, const void *v_new, int64_t ld_kv,
                       int32_t s_begin, int32_t s_count, void *stream);
 
 /* Decode attention at step t over the slots present (the cache already holds
- * token t).  out row of stream s at out + s*ld_o.  For Global streams the
- * softmax probabilities are added to score (written instead of added at the
- * first query of each scoring window). */
+ * token t): out row of stream s at out + s*ld_o, q row at q + s*ld_q. */
 hkv_status hkv_decode_attn(const hkv_config *cfg, hkv_state *st, int32_t t,
                            const void *q, int64_t ld_q, void *out, int64_t ld_o,
                            int32_t s_begin, int32_t s_count, void *stream);
 
-/* STE at step t for every Global stream of the range whose count reached
- * budget + M: evict M, tail-fill, count = budget.  evicted_pos_log (optional,
- * device, [S, M] int32): evicted positions in ascending slot order, or -1 for
- * streams that did not evict. */
+/* STE at step t for every Global stream of the range holding budget + M
+ * tokens: score the slots, evict M (floor(M/2) near, the rest far) and free
+ * their slots (free_slots, n_free = M; no row moves).
+ *   q_win: the W most recent queries (positions t-W+1 .. t, oldest first) of
+ *          stream s at q_win + s*ld_qw + r*head_dim.  A slot's score is the sum
+ *          over these queries of the softmax probability it receives, each query
+ *          attending to the slots whose position does not exceed its own — the
+ *          probabilities the slot received during the last W decode steps.
+ *          NULL: the scores are taken from st->score as stored by the caller.
+ *   evicted_pos_log (optional, device, [S, M] int32): evicted positions in
+ *          ascending slot order, -1 for streams that did not evict.
+ * With a log, an eviction also writes the scores of every slot to st->score
+ * (0 for the freed ones). */
 hkv_status hkv_ste_evict(const hkv_config *cfg, hkv_state *st, int32_t t,
-                         int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
-                         void *stream);
+                         const void *q_win, int64_t ld_qw, int32_t *evicted_pos_log,
+                         int32_t s_begin, int32_t s_count, void *stream);
 
-/* One decode step in a single launch: exactly hkv_append, then hkv_decode_attn,
- * then hkv_ste_evict, with identical results (bit for bit). */
+/* One decode step in a single launch: exactly hkv_append, then hkv_decode_attn
+ * with the newest query of the window (row W-1), then hkv_ste_evict with the
+ * window, with identical results (bit for bit). */
 hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
                            const void *k_new, const void *v_new, int64_t ld_kv,
-                           const void *q, int64_t ld_q, void *out, int64_t ld_o,
+                           const void *q_win, int64_t ld_qw, void *out, int64_t ld_o,
                            int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
                            void *stream);
 

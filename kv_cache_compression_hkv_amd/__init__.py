@@ -46,8 +46,9 @@ class hkv_state(ctypes.Structure):
     _fields_ = [("k_pool", c_void_p), ("v_pool", c_void_p), ("pos", c_void_p),
                 ("score", c_void_p), ("base", c_void_p), ("cap", c_void_p),
                 ("count", c_void_p), ("budget", c_void_p), ("n_tokens", c_void_p),
-                ("label", c_void_p), ("err", c_void_p), ("workspace", c_void_p),
-                ("workspace_bytes", c_size_t), ("phase", c_int32)]
+                ("label", c_void_p), ("free_slots", c_void_p), ("n_free", c_void_p),
+                ("err", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
+                ("phase", c_int32)]
 
 
 class HkvError(RuntimeError):
@@ -72,7 +73,8 @@ def _load():
                                  c_int32, c_void_p]),
         "hkv_decode_attn": (c_int32, [cfgp, stp, c_int32, c_void_p, c_int64, c_void_p, c_int64,
                                       c_int32, c_int32, c_void_p]),
-        "hkv_ste_evict": (c_int32, [cfgp, stp, c_int32, c_void_p, c_int32, c_int32, c_void_p]),
+        "hkv_ste_evict": (c_int32, [cfgp, stp, c_int32, c_void_p, c_int64, c_void_p, c_int32,
+                                    c_int32, c_void_p]),
         "hkv_decode_step": (c_int32, [cfgp, stp, c_int32, c_void_p, c_void_p, c_int64, c_void_p,
                                       c_int64, c_void_p, c_int64, c_void_p, c_int32, c_int32,
                                       c_void_p]),
@@ -171,16 +173,17 @@ def hkv_decode_attn(cfg, state, t, q, ld_q, out, ld_o, s_begin, s_count, stream=
                  _ptr(out), ld_o, s_begin, s_count, _stream(stream))
 
 
-def hkv_ste_evict(cfg, state, t, evicted_pos_log, s_begin, s_count, stream=None):
-    return _call("hkv_ste_evict", ctypes.byref(cfg), ctypes.byref(state), t,
-                 _ptr(evicted_pos_log), s_begin, s_count, _stream(stream))
+def hkv_ste_evict(cfg, state, t, q_win, ld_qw, evicted_pos_log, s_begin, s_count,
+                  stream=None):
+    return _call("hkv_ste_evict", ctypes.byref(cfg), ctypes.byref(state), t, _ptr(q_win),
+                 ld_qw, _ptr(evicted_pos_log), s_begin, s_count, _stream(stream))
 
 
-def hkv_decode_step(cfg, state, t, k_new, v_new, ld_kv, q, ld_q, out, ld_o, evicted_pos_log,
-                    s_begin, s_count, stream=None):
+def hkv_decode_step(cfg, state, t, k_new, v_new, ld_kv, q_win, ld_qw, out, ld_o,
+                    evicted_pos_log, s_begin, s_count, stream=None):
     return _call("hkv_decode_step", ctypes.byref(cfg), ctypes.byref(state), t, _ptr(k_new),
-                 _ptr(v_new), ld_kv, _ptr(q), ld_q, _ptr(out), ld_o, _ptr(evicted_pos_log),
-                 s_begin, s_count, _stream(stream))
+                 _ptr(v_new), ld_kv, _ptr(q_win), ld_qw, _ptr(out), ld_o,
+                 _ptr(evicted_pos_log), s_begin, s_count, _stream(stream))
 
 
 def hkv_check(cfg, state, stream=None):
@@ -210,6 +213,8 @@ class HkvCache:
         self.budget = torch.zeros((S,), dtype=torch.int32, device=dev)
         self.n_tokens = torch.zeros((S,), dtype=torch.int32, device=dev)
         self.label = torch.zeros((S,), dtype=torch.uint8, device=dev)
+        self.free_slots = torch.zeros((S, max(1, cfg.evict_m)), dtype=torch.int32, device=dev)
+        self.n_free = torch.zeros((S,), dtype=torch.int32, device=dev)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
         nbytes = hkv_workspace_bytes(cfg)
         self.workspace = torch.zeros((nbytes + 256,), dtype=torch.uint8, device=dev)
@@ -219,4 +224,5 @@ class HkvCache:
             self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.pos.data_ptr(),
             self.score.data_ptr(), self.base.data_ptr(), self.cap.data_ptr(),
             self.count.data_ptr(), self.budget.data_ptr(), self.n_tokens.data_ptr(),
-            self.label.data_ptr(), self.err.data_ptr(), ws_aligned, nbytes, 0)
+            self.label.data_ptr(), self.free_slots.data_ptr(), self.n_free.data_ptr(),
+            self.err.data_ptr(), ws_aligned, nbytes, 0)

@@ -74,10 +74,14 @@ hkv_status derive(const hkv_config* c, Derived* d) {
   size_t off = 0;
   d->ws_init_scores = off;
   off = align256(off + size_t(S) * size_t(c->prefill_len) * sizeof(float));
-  d->ws_logits = off;
-  off = align256(off + size_t(d->pool_slots) * sizeof(float));
+  d->ws_tile = off;
+  off = align256(off + size_t(d->pool_slots) * size_t(c->w_obs) * sizeof(float));
+  d->ws_pos = off;
+  off = align256(off + size_t(d->pool_slots) * sizeof(int32_t));
   d->ws_keys = off;
   off = align256(off + size_t(d->pool_slots) * sizeof(uint64_t));
+  d->ws_evf = off;
+  off = align256(off + size_t(d->pool_slots));
   d->ws_bytes = off;
   return HKV_OK;
 }
@@ -85,14 +89,16 @@ hkv_status derive(const hkv_config* c, Derived* d) {
 hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st) {
   if (!st) return fail(HKV_E_INVAL, "state is NULL");
   if (!st->k_pool || !st->v_pool || !st->pos || !st->score || !st->base || !st->cap ||
-      !st->count || !st->budget || !st->n_tokens || !st->label || !st->err)
+      !st->count || !st->budget || !st->n_tokens || !st->label || !st->err ||
+      !st->free_slots || !st->n_free)
     return fail(HKV_E_INVAL, "state has a NULL buffer");
   if (!aligned16(st->k_pool) || !aligned16(st->v_pool))
     return fail(HKV_E_INVAL, "k_pool/v_pool must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(st->base) & 7u) || (reinterpret_cast<uintptr_t>(st->pos) & 3u) ||
       (reinterpret_cast<uintptr_t>(st->score) & 3u) || (reinterpret_cast<uintptr_t>(st->label) & 3u) ||
       (reinterpret_cast<uintptr_t>(st->count) & 3u) || (reinterpret_cast<uintptr_t>(st->cap) & 3u) ||
-      (reinterpret_cast<uintptr_t>(st->budget) & 3u) || (reinterpret_cast<uintptr_t>(st->n_tokens) & 3u))
+      (reinterpret_cast<uintptr_t>(st->budget) & 3u) || (reinterpret_cast<uintptr_t>(st->n_tokens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(st->free_slots) & 3u) || (reinterpret_cast<uintptr_t>(st->n_free) & 3u))
     return fail(HKV_E_INVAL, "state index buffers misaligned");
   Derived d;
   hkv_status s = derive(c, &d);

@@ -12,8 +12,8 @@ namespace hkv {
 
 // Limits of this implementation (checked by hkv_validate).
 constexpr int kMaxPrefill = 1024;   // classification keeps W x P logits on chip
-constexpr int kMaxWobs = 16;        // observation queries held per lane
-constexpr int kMaxEvict = 64;       // evictions per decode event
+constexpr int kMaxWobs = 8;         // observation / scoring window queries
+constexpr int kMaxEvict = 8;        // evictions per decode event (M = W)
 constexpr int kMaxHeads = 1024;
 
 struct Derived {
@@ -23,8 +23,10 @@ struct Derived {
   int64_t pool_slots = 0;
   // workspace layout (bytes from the workspace start, 256-B aligned)
   size_t ws_init_scores = 0;   // float [S * P]
-  size_t ws_logits = 0;        // float [pool_slots]
+  size_t ws_tile = 0;          // float [pool_slots * w_obs]
+  size_t ws_pos = 0;           // int32 [pool_slots]
   size_t ws_keys = 0;          // uint64 [pool_slots]
+  size_t ws_evf = 0;           // uint8 [pool_slots]
   size_t ws_bytes = 0;
 };
 

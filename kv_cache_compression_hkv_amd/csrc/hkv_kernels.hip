@@ -28,15 +28,15 @@ namespace hkv {
 namespace dev {
 
 // Tuning knobs (compile-time): waves per workgroup, row fragments in flight per
-// lane, prefetched score slots per thread, minimum waves per SIMD.
+// lane, minimum waves per SIMD.
 #ifndef HKV_NW
 #define HKV_NW 4
 #endif
 #ifndef HKV_U
 #define HKV_U 2
 #endif
-#ifndef HKV_KPT
-#define HKV_KPT 1
+#ifndef HKV_UT
+#define HKV_UT 1
 #endif
 #ifndef HKV_WPE
 #define HKV_WPE 1
@@ -46,15 +46,17 @@ constexpr int kNT = kNW * kWave;
 
 struct StepArgs {
   const char* k_new; const char* v_new; long long ld_kv;   // ld in elements
-  const char* q; long long ld_q;
+  const char* q; long long ld_q;                            // current query
+  const char* q_win; long long ld_qw;                       // last W queries, oldest first
   char* out; long long ld_o;
   int* log;
   char* k_pool; char* v_pool;
   int* pos; float* score;
   const long long* base; int* count; const int* budget; const int* cap;
   const unsigned char* label;
+  int* free_slots; int* n_free;
   int* err;
-  float* ws_logits; uint64_t* ws_keys;
+  float* ws_tile; int* ws_pos; uint64_t* ws_keys; uint8_t* ws_evf;   // per-slot spill
   int s_begin, t, w, W, M, D;
   int S;                               // streams in the state (label array length)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
@@ -68,9 +70,8 @@ struct CombineShared {
 
 struct EvictShared {
   int cnt[2];
-  int nh, nm, ne;
-  int holes[kMaxEvict], movers[kMaxEvict];
-  int mover_rank[kMaxEvict];           // tail slot B + r -> mover index, or -1
+  int ne;
+  float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / sum of each window query
 };
 
 // Eviction key with the subset in the top bits: (subset << 62) | (score bits <<
@@ -84,63 +85,477 @@ __device__ inline int skey_sub(uint64_t k) { return int(k >> 62); }
 __device__ inline int skey_pos(uint64_t k) { return int(uint32_t(k) & 0x7fffffffu); }
 __device__ inline float skey_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 31) & 0x7fffffffu); }
 
-// Source of fragment idx of the tail rows [B, B + M): row B + idx / (2G), K
-// (first G fragments of the row) or V, 16-byte piece idx % G; the token appended
-// in this launch is read from its source row.
-template <class T, int D, bool AP>
-__device__ inline const char* tail_src_impl(const StepArgs& a, int s, long long base,
-                                            int slot_new, int B, int idx) {
-  constexpr int VE = Frag<T>::N, G = D / VE, ES = sizeof(T);
-  const int row = B + idx / (2 * G);
-  const bool isv = (idx % (2 * G)) >= G;
-  const int sb = idx % G;
-  if (AP && row == slot_new)
-    return (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sb * VE) * ES;
-  return (isv ? a.v_pool : a.k_pool) + ((base + row) * D + sb * VE) * ES;
-}
-
-// Body of a decode step for one stream after its metadata is known.  `lg`,
-// `keys` and `evf` are per-slot scratch: on chip (LDS) for streams of at most
-// kLdsSlots slots, else in the workspace; instantiating both cases lets the
-// compiler address the on-chip case with LDS instructions.
 struct StepCtx {
   long long base;
-  int s, lab, c, B, slot_new;
-  bool glob, write_mode, due;
+  int s, lab, c, B, slot_new;          // c: slots holding a token (no free slot when due)
+  bool glob, due;
 };
 
+// Per-slot scratch of an eviction: the W x c score tile (aliased by the keys
+// once the scores are formed), positions and eviction flags.  On chip (LDS)
+// for streams of at most kLdsSlots slots, else in the workspace; instantiating
+// both cases lets the compiler address the on-chip case with LDS instructions.
+struct Scratch {
+  float* tile;
+  int* pos;
+  uint64_t* keys;
+  uint8_t* evf;
+};
+
+// ------------------------------------------------------------------ eviction
+// Stratified Token Eviction of one due Global stream (c == B + M slots):
+//   1. scores: with a query window, the causal W x c probability tile of the
+//      last W queries (query i at position t-W+1+i sees slots with pos <= its
+//      position), summed over the queries; without one, the state's scores;
+//   2. keys (subset, score, position); near/far sizes and quotas;
+//   3. rank of every candidate inside its subset; evicted iff rank < quota;
+//   4. the evicted slots are freed (position -1, listed ascending in the free
+//      list for the next appends); no row moves.  Returns n_free = M.
+template <class T, int D, bool AP>
+__device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
+                                            EvictShared& es, bool tile_ready) {
+  // (returns the number of freed slots: M, or 0 if nothing was evicted)
+  using F = Frag<T>;
+  constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane / G, sub = lane % G;
+  const long long base = x.base;
+  const int s = x.s, c = x.c, slot_new = x.slot_new;
+  const int t = a.t, W = a.W, Dd = a.D;
+
+  if (tid < 2) es.cnt[tid] = 0;
+
+  // positions of all slots (already staged by the attention when tile_ready)
+  if (!tile_ready)
+    for (int j = tid; j < c; j += kNT) sc.pos[j] = (AP && j == slot_new) ? t : a.pos[base + j];
+
+  const bool window = a.q_win != nullptr;
+  if (window && tile_ready) {
+    // the W x c tile was produced by the attention's matrix-core pass
+  } else if (window) {
+    if constexpr (sizeof(T) == 2) {
+      // bf16: the W x c logit tile on the matrix cores.  v_mfma_f32_16x16x32_bf16:
+      // A = the W queries (rows W..15 zero), B = 16 keys per tile, K = 32 head
+      // elements per instruction; lane l holds A row l%16 and B column l%16 at
+      // elements (l/16)*8 .. +7, and receives D rows (l/16)*4 .. +3, column l%16.
+      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      constexpr int KC = D / 32;
+      const int li = lane % 16, lk = lane / 16;
+      bf16x8 qa[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (li < W)
+          u = ld16(a.q_win + ((long long)s * a.ld_qw + (long long)li * D + lk * 8 + kc * 32) * ES);
+        qa[kc] = __builtin_bit_cast(bf16x8, u);
+      }
+      const char* knew = a.k_new + ((long long)s * a.ld_kv) * ES;
+      const int ntile = (c + 15) / 16;
+      for (int kt = wave; kt < ntile; kt += kNW) {
+        const int j = kt * 16 + li;
+        const char* row = (AP && j == slot_new) ? knew : a.k_pool + ((base + j) * D) * ES;
+        uint4 kb[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          kb[kc] = j < c ? ld16(row + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[kc]),
+                                                        acc, 0, 0, 0);
+        if (j < c) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = lk * 4 + r;
+            if (i < W) sc.tile[i * c + j] = acc[r] * a.scale_log2;
+          }
+        }
+      }
+    } else {
+      // fp32: each lane keeps its fragment of every window query in registers
+      float qf[kMaxWobs][VE];
+#pragma unroll
+      for (int i = 0; i < kMaxWobs; ++i) {
+        float tmp[VE];
+        if (i < W) {
+          F::to_f32(ld16(a.q_win + ((long long)s * a.ld_qw + (long long)i * D + sub * VE) * ES), tmp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) tmp[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) qf[i][e] = tmp[e] * a.scale_log2;
+      }
+      const char* kbase = a.k_pool + (base * D + sub * VE) * ES;
+      const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
+      for (int j0 = wave * R; j0 < c; j0 += kNW * R) {
+        const int j = j0 + g;
+        if (j < c) {
+          float kf[VE];
+          F::to_f32(ld16((AP && j == slot_new) ? knew : kbase + (long long)j * D * ES), kf);
+          float mine = 0.f;
+#pragma unroll
+          for (int i = 0; i < kMaxWobs; ++i) {
+            float d0 = 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) d0 = fmaf(qf[i][e], kf[e], d0);
+            d0 = group_sum<G>(d0);
+            if (i == sub) mine = d0;
+          }
+          if (sub < W) sc.tile[sub * c + j] = mine;
+        }
+      }
+    }
+  }
+  if (window) {
+    __syncthreads();
+    // softmax statistics of each window query over the slots it sees
+    for (int i = wave; i < W; i += kNW) {
+      const int lim = t - W + 1 + i;
+      float m = kNeg;
+      for (int j = lane; j < c; j += kWave)
+        if (sc.pos[j] <= lim) m = fmaxf(m, sc.tile[i * c + j]);
+      m = wave_max(m);
+      float l = 0.f;
+      for (int j = lane; j < c; j += kWave)
+        if (sc.pos[j] <= lim) l += exp2f(sc.tile[i * c + j] - m);
+      l = wave_sum(l);
+      if (lane == 0) {
+        es.qm[i] = m;
+        es.ql[i] = l;
+      }
+    }
+    __syncthreads();
+  } else {
+    __syncthreads();
+  }
+
+  // scores -> keys (the keys overwrite the tile: read first, then write)
+  constexpr int SPT = (kLdsSlots + kNT - 1) / kNT;
+  float scv[SPT];
+  int nn = 0, nf = 0;
+  for (int k = 0, j = tid; k < SPT || j < c; ++k, j += kNT) {
+    if (j >= c) break;
+    float v = 0.f;
+    if (window) {
+      const int pj = sc.pos[j];
+      for (int i = 0; i < W; ++i)
+        if (pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * (1.0f / es.ql[i]);
+    } else {
+      v = (AP && j == slot_new) ? 0.0f : a.score[base + j];
+    }
+    if (k < SPT) {
+#pragma unroll
+      for (int kk = 0; kk < SPT; ++kk)
+        if (kk == k) scv[kk] = v;
+    } else {
+      // streams beyond the on-chip size keep keys apart from the tile
+      const int pj = sc.pos[j];
+      const int dist = t - pj;
+      const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
+      nn += sb == 0;
+      nf += sb == 1;
+      sc.keys[j] = make_skey(sb, v, pj);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int j = tid + k * kNT;
+    if (j < c) {
+      const int pj = sc.pos[j];
+      const int dist = t - pj;
+      const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
+      nn += sb == 0;
+      nf += sb == 1;
+      sc.keys[j] = make_skey(sb, scv[k], pj);
+    }
+  }
+  nn = wave_sum_int(nn);
+  nf = wave_sum_int(nf);
+  if (lane == 0) {
+    if (nn) atomicAdd(&es.cnt[0], nn);
+    if (nf) atomicAdd(&es.cnt[1], nf);
+  }
+  __syncthreads();
+
+  // quotas: floor(M/2) near, the rest far; a short subset gives all it has
+  const int E = a.M;
+  const int n_near = es.cnt[0], n_far = es.cnt[1];
+  int qn = E / 2, qf = E - qn;
+  if (n_near < qn) {
+    qn = n_near;
+    qf = E - qn;
+  } else if (n_far < qf) {
+    qf = n_far;
+    qn = E - qf;
+  }
+  if (qn > n_near || qf > n_far) {
+    if (tid == 0) atomicOr(a.err, HKV_ERRBIT_SELECT);
+    if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
+    return 0;
+  }
+  // rank of each candidate inside its subset (one key range per subset)
+  for (int j = tid; j < c; j += kNT) {
+    const uint64_t kj = sc.keys[j];
+    const int sb = skey_sub(kj);
+    const uint64_t lo = uint64_t(sb & 1) << 62;
+    int r = 0, i = 0;
+    for (; i + 8 <= c; i += 8) {
+      uint64_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kk[u] = sc.keys[i + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (kk[u] >= lo) & (kk[u] < kj);
+    }
+    for (; i < c; ++i) {
+      const uint64_t ki = sc.keys[i];
+      r += (ki >= lo) & (ki < kj);
+    }
+    sc.evf[j] = (sb < 2 && r < (sb == 0 ? qn : qf)) ? 1 : 0;
+  }
+  __syncthreads();
+  // the evicted slots, ascending: free list, log, positions
+  if (wave == 0) {
+    int ne = 0;
+    const uint64_t lt = lanemask_lt(lane);
+    for (int j0 = 0; j0 < c; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool ev = j < c && sc.evf[j];
+      const uint64_t me = __ballot(ev);
+      if (ev) {
+        const int r = ne + __popcll(me & lt);
+        if (r < a.M) {
+          a.free_slots[(long long)s * a.M + r] = j;
+          if (a.log) a.log[(long long)s * a.M + r] = skey_pos(sc.keys[j]);
+        }
+        a.pos[base + j] = -1;
+      }
+      ne += __popcll(me);
+    }
+    if (lane == 0) es.ne = ne;
+    if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
+  }
+  // with a log, the scores of the event (0 for the freed slots)
+  if (a.log)
+    for (int j = tid; j < c; j += kNT) a.score[base + j] = sc.evf[j] ? 0.0f : skey_score(sc.keys[j]);
+  __syncthreads();
+  if (es.ne != a.M) {
+    if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
+    return 0;
+  }
+  return a.M;
+}
+
+// ------------------------------------------------------------------ attention (bf16)
+// Flash-decode over the slots [0, c) of one stream with the logits on the matrix
+// cores.  v_mfma_f32_16x16x32_bf16 with A = queries (16 rows), B = 16 keys: rows
+// 3, 7, 11 and 15 of A hold the current query, so every lane receives the
+// current logit of its key column in D[.][3]; on an eviction step the other
+// rows hold the W-1 earlier window queries (row (i/3)*4 + i%3 for query i) and
+// the W x c scoring tile comes out of the same instructions.  Lane l holds key
+// column l%16 and head elements (l/16)*8 + 32*kc .. +7 of K and V; softmax and
+// P.V run per lane on its column and are reduced over the 16 columns at the end.
+template <int D, bool AP>
+__device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x, bool due,
+                                            Scratch sc, CombineShared& cs) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  using F = Frag<uint16_t>;
+  constexpr int KC = D / 32, ES = 2;
+  constexpr int UT = HKV_UT;                    // key tiles in flight per wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const long long base = x.base;
+  const int s = x.s, c = x.c, slot_new = x.slot_new, W = a.W;
+
+  // A operand: the query of row li
+  const char* qsrc = nullptr;
+  if ((li & 3) == 3) {
+    qsrc = a.q + (long long)s * a.ld_q * ES;
+  } else if (due) {
+    const int i = (li >> 2) * 3 + (li & 3);
+    if (i < W - 1) qsrc = a.q_win + ((long long)s * a.ld_qw + (long long)i * D) * ES;
+  }
+  bf16x8 qa[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+    qa[kc] = __builtin_bit_cast(bf16x8, qsrc ? ld16(qsrc + (lk * 8 + kc * 32) * ES)
+                                             : make_uint4(0, 0, 0, 0));
+
+  const char* knew = a.k_new + (long long)s * a.ld_kv * ES;
+  const char* vnew = a.v_new + (long long)s * a.ld_kv * ES;
+  const int ntile = (c + 15) >> 4;
+  const int per = (ntile + kNW - 1) / kNW;
+  const int t0 = wave * per;
+  const int t1 = min(ntile, t0 + per);
+
+  float m_run = kNeg, l_run = 0.f;
+  float acc[KC][8];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[kc][e] = 0.f;
+
+  for (int tt = t0; tt < t1; tt += UT) {
+    uint4 kb[UT][KC], vb[UT][KC];
+    int pv[UT];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int j = (tt + u) * 16 + li;
+      const bool valid = (tt + u < t1) && j < c;
+      const bool fresh = AP && j == slot_new;
+      const char* kr = fresh ? knew : a.k_pool + (base + j) * D * ES;
+      const char* vr = fresh ? vnew : a.v_pool + (base + j) * D * ES;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        kb[u][kc] = valid ? ld16(kr + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
+        vb[u][kc] = valid ? ld16(vr + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
+      }
+      pv[u] = 0;
+      if (due && lk == 0 && valid) pv[u] = fresh ? a.t : a.pos[base + j];
+    }
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int j = (tt + u) * 16 + li;
+      const bool valid = (tt + u < t1) && j < c;
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[u][kc]),
+                                                    S, 0, 0, 0);
+      const float cur = S[3] * a.scale_log2;
+      if (due && valid) {
+        if (lk == 0) {
+          sc.tile[(W - 1) * c + j] = cur;
+          sc.pos[j] = pv[u];
+        }
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          const int i = lk * 3 + r;
+          if (i < W - 1) sc.tile[i * c + j] = S[r] * a.scale_log2;
+        }
+      }
+      const float sv = valid ? cur : kNeg;
+      const float m_new = fmaxf(m_run, sv);
+      const float alpha = exp2f(m_run - m_new);
+      const float p = valid ? exp2f(sv - m_new) : 0.f;
+      l_run = fmaf(l_run, alpha, p);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        float vf[8];
+        F::to_f32(vb[u][kc], vf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[kc][e] = fmaf(p, vf[e], acc[kc][e] * alpha);
+      }
+      m_run = m_new;
+    }
+  }
+  // reduce over the 16 key columns of each 16-lane row
+  float m_w = m_run;
+  m_w = fmaxf(m_w, dpp<0xB1>(m_w));
+  m_w = fmaxf(m_w, dpp<0x4E>(m_w));
+  m_w = fmaxf(m_w, dpp<0x141>(m_w));
+  m_w = fmaxf(m_w, dpp<0x140>(m_w));
+  const float f = exp2f(m_run - m_w);
+  const float l_w = group_sum<16>(l_run * f);
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[kc][e] = group_sum<16>(acc[kc][e] * f);
+  if (li == 0) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs.o[wave][lk * 8 + kc * 32 + e] = acc[kc][e];
+    if (lk == 0) {
+      cs.m[wave] = m_w;
+      cs.l[wave] = l_w;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ k_step
+// One workgroup per stream: append token t (optional), attend over the slots
+// present (optional) and, if the stream is a Global stream at B + M slots, evict
+// (optional) — one launch.  Every thread reads the stream's metadata itself
+// (uniform scalar loads, no barrier); the query is requested first.
 template <class T, int D, bool AP, bool AT, bool EV>
-__device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, uint4 q_raw,
-                                          float* lg, uint64_t* keys, uint8_t* evf,
-                                          CombineShared& cs, EvictShared& es) {
+__global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
   using F = Frag<T>;
   constexpr int VE = F::N;           // elements per 16-byte fragment
   constexpr int G = D / VE;          // lanes per row
   constexpr int R = kWave / G;       // rows per wave instruction
   constexpr int U = HKV_U;           // row fragments in flight per lane
   constexpr int ES = sizeof(T);
-  constexpr int KPT = HKV_KPT;       // prefetched score slots per thread
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane / G, sub = lane % G;
-  const long long base = x.base;
-  const int s = x.s, c = x.c, B = x.B, slot_new = x.slot_new;
-  const bool glob = x.glob, write_mode = x.write_mode, due = x.due;
-  auto tail_src = [](const StepArgs& aa, int ss, long long bb, int sn, int BB, int idx) {
-    return tail_src_impl<T, D, AP>(aa, ss, bb, sn, BB, idx);
-  };
 
-  // prefetch the score window and, on an eviction step, the positions
-  float sc_old[KPT > 0 ? KPT : 1];
-  int pos_old[KPT > 0 ? KPT : 1];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int j = tid + k * kNT;
-    const bool fresh = AP && j == slot_new;
-    sc_old[k] = 0.f;
-    pos_old[k] = 0;
-    if (j < c && glob && !fresh && (due || (AT && !write_mode))) sc_old[k] = a.score[base + j];
-    if (j < c && due) pos_old[k] = fresh ? a.t : a.pos[base + j];
+  __shared__ CombineShared cs;
+  __shared__ EvictShared es;
+  __shared__ float lds_tile[EV ? kMaxWobs * kLdsSlots : 1];   // W x c floats, then keys
+  __shared__ int lds_pos[EV ? kLdsSlots : 1];
+  __shared__ uint8_t lds_evf[EV ? kLdsSlots : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = a.s_begin + blockIdx.x;
+  const int g = lane / G, sub = lane % G;
+
+  constexpr bool kMfma = sizeof(T) == 2;     // bf16: eviction steps attend on the matrix cores
+  // query fragment first: its address does not depend on the stream metadata
+  uint4 q_raw = make_uint4(0, 0, 0, 0);
+  if (AT) q_raw = ld16(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
+
+  // the label byte through the scalar path (aligned 32-bit word), except in a
+  // last partial word
+  int lab;
+  if (4LL * ((s >> 2) + 1) <= a.S)
+    lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
+  else
+    lab = a.label[s];
+  const int ext0 = a.count[s];               // table extent (slots in use incl. freed)
+  const int capv = a.cap[s];
+  const int B = a.budget[s];
+  const long long base = a.base[s];
+  const bool glob = lab == HKV_GLOBAL;
+  const int nf0 = glob ? a.n_free[s] : 0;     // freed slots not yet refilled
+  int ext = ext0, nf = nf0, slot_new = -1;
+  bool ok = nf0 >= 0 && nf0 <= a.M;
+  if (ok && AP) {
+    if (lab == HKV_LOCAL) {
+      slot_new = a.t % a.w;
+      ext = ext0 + 1 < a.w ? ext0 + 1 : a.w;
+    } else if (nf0 > 0) {                     // lowest freed slot
+      slot_new = a.free_slots[(long long)s * a.M + (a.M - nf0)];
+      nf = nf0 - 1;
+      ok = slot_new >= 0 && slot_new < ext0;
+    } else {
+      slot_new = ext0;
+      ext = ext0 + 1;
+      if (ext0 >= capv) {
+        ok = false;
+        if (tid == 0) atomicOr(a.err, HKV_ERRBIT_CAPACITY);
+      }
+    }
   }
+  const int c = ext - nf;                     // slots holding a token
+  if (ok && (c < 1 || ext > capv || lab > HKV_FULL)) ok = false;
+  if (!ok) {
+    if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
+    if (EV && a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
+    return;
+  }
+  const bool due = EV && glob && (c == B + a.M);
+  // freed slots still empty: the last nf entries of the stream's free list
+  int fr[kMaxEvict];
+#pragma unroll
+  for (int k = 0; k < kMaxEvict; ++k)
+    fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
+  auto is_free = [&](int row) {
+    bool f = false;
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k) f |= (row == fr[k]);
+    return f;
+  };
 
   // ---------------- append token t
   if (AP) {
@@ -153,13 +568,38 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
     }
     if (tid == 0) {
       a.pos[base + slot_new] = a.t;
-      if (glob && !AT) a.score[base + slot_new] = 0.0f;
+      if (glob) a.score[base + slot_new] = 0.0f;
     }
   }
 
+  // eviction scratch of a due stream: on chip up to kLdsSlots slots
+  const bool onchip = c <= kLdsSlots;
+  Scratch scr_l{lds_tile, lds_pos, reinterpret_cast<uint64_t*>(lds_tile), lds_evf};
+  Scratch scr_g{a.ws_tile + base * a.W, a.ws_pos + base, a.ws_keys + base, a.ws_evf + base};
+  StepCtx x;
+  x.base = base;
+  x.s = s;
+  x.lab = lab;
+  x.c = c;
+  x.B = B;
+  x.slot_new = slot_new;
+  x.glob = glob;
+  x.due = due;
+
   // ---------------- attention over slots [0, c)
-  float Mx = 0.f, inv_l = 0.f;
-  if (AT) {
+  // A bf16 Global stream at its eviction point (c == B + M) attends on the
+  // matrix cores — in the fused step this also yields its W x c scoring tile;
+  // every other stream attends on the vector ALUs.  The choice depends on the
+  // stream state only, so standalone and fused attention give identical bits.
+  const bool at_point = kMfma && AT && glob && c == B + a.M;
+  const bool tile_here = at_point && EV && due && a.q_win != nullptr;
+  if (at_point) {
+    if (onchip)
+      attend_mfma<D, AP>(a, x, tile_here, scr_l, cs);
+    else
+      attend_mfma<D, AP>(a, x, tile_here, scr_g, cs);
+  }
+  if (AT && !at_point) {
     float qv[VE];
     {
       float qf[VE];
@@ -172,7 +612,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
     const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
     const char* vnew = a.v_new + ((long long)s * a.ld_kv + sub * VE) * ES;
 
-    const int ntiles = (c + R - 1) / R;
+    const int ntiles = (ext + R - 1) / R;
     const int per = (ntiles + kNW - 1) / kNW;
     const int t0 = wave * per;
     const int t1 = min(ntiles, t0 + per);
@@ -188,7 +628,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = (tt + u) * R + g;
-        valid[u] = (tt + u < t1) && row < c;
+        valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
         if (valid[u]) {
@@ -197,7 +637,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
           vr[u] = ld16(fresh ? vnew : vbase + (long long)row * D * ES);
         }
       }
-      float sc[U];
+      float scr[U];
       float m_tile = kNeg;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -207,9 +647,8 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
 #pragma unroll
         for (int i = 0; i < VE; ++i) d0 = fmaf(qv[i], kf[i], d0);
         d0 = group_sum<G>(d0);
-        sc[u] = valid[u] ? d0 : kNeg;
-        m_tile = fmaxf(m_tile, sc[u]);
-        if (glob && sub == 0 && valid[u]) lg[(tt + u) * R + g] = d0;
+        scr[u] = valid[u] ? d0 : kNeg;
+        m_tile = fmaxf(m_tile, scr[u]);
       }
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = exp2f(m_run - m_new);
@@ -218,7 +657,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
       for (int i = 0; i < VE; ++i) acc[i] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float p = valid[u] ? exp2f(sc[u] - m_new) : 0.f;
+        const float p = valid[u] ? exp2f(scr[u] - m_new) : 0.f;
         l_run += p;
         float vf[VE];
         F::to_f32(vr[u], vf);
@@ -241,285 +680,44 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepCtx& x, u
         cs.l[wave] = l_run;
       }
     }
-    __syncthreads();
-    // combine the waves
-    Mx = cs.m[0];
-#pragma unroll
-    for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
-    float L = 0.f, fw[kNW];
-#pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) {
-      fw[w2] = exp2f(cs.m[w2] - Mx);
-      L += cs.l[w2] * fw[w2];
-    }
-    inv_l = 1.0f / L;
-    if (tid < D) {
-      float o = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2) o = fmaf(cs.o[w2][tid], fw[w2], o);
-      T* op = reinterpret_cast<T*>(a.out + ((long long)s * a.ld_o) * ES);
-      op[tid] = F::from_f32(o * inv_l);
-    }
   }
-
-  // ---------------- score side-output (Global streams) / eviction keys
-  if (!AT && due) __syncthreads();                     // counters zeroed
-  if (glob && (AT || due)) {
-    const int t = a.t, W = a.W, Dd = a.D;
-    int nn = 0, nf = 0;
-    auto handle = [&](int j, float old, int pos_j) {
-      const bool fresh = AP && j == slot_new;
-      float ns = old;
-      if (AT) {
-        const float p = exp2f(lg[j] - Mx) * inv_l;
-        ns = (fresh || write_mode) ? p : old + p;
-      } else if (fresh) {
-        ns = 0.0f;
-      }
-      if (due) {
-        const int dist = t - pos_j;
-        const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
-        nn += sb == 0;
-        nf += sb == 1;
-        keys[j] = make_skey(sb, ns, pos_j);
-      } else {
-        a.score[base + j] = ns;
-      }
-    };
+  if (AT) {
+    // combine the waves
+    __syncthreads();
+    if (tid < D) {
+      float Mx = cs.m[0];
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int j = tid + k * kNT;
-      if (j < c) handle(j, sc_old[k], pos_old[k]);
-    }
-    for (int j = tid + KPT * kNT; j < c; j += kNT) {
-      const bool fresh = AP && j == slot_new;
-      const float old = (!fresh && (due || !write_mode)) ? a.score[base + j] : 0.f;
-      handle(j, old, due ? (fresh ? a.t : a.pos[base + j]) : 0);
-    }
-    if (due) {
-      nn = wave_sum_int(nn);
-      nf = wave_sum_int(nf);
-      if (lane == 0) {
-        if (nn) atomicAdd(&es.cnt[0], nn);
-        if (nf) atomicAdd(&es.cnt[1], nf);
+      for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
+      float L = 0.f, o = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2) {
+        const float fw = exp2f(cs.m[w2] - Mx);
+        L = fmaf(cs.l[w2], fw, L);
+        o = fmaf(cs.o[w2][tid], fw, o);
       }
+      T* op = reinterpret_cast<T*>(a.out + ((long long)s * a.ld_o) * ES);
+      op[tid] = F::from_f32(o / L);
     }
   }
 
   // ---------------- Stratified Token Eviction (due Global streams)
-  int c_final = c;
-  if (EV && due) {
-    // Every mover lies in the tail [B, c) (c - B = M on an eviction step): fetch
-    // those rows now so the loads overlap the selection.  Fragment idx of the
-    // tail: row B + idx / (2G), K or V, 16-byte piece idx % G.
-    constexpr int MVF = 2;                             // fragments fetched per thread
-    const int n_frag = 2 * G * (c - B);
-    uint4 mv_frag[MVF];
-#pragma unroll
-    for (int f = 0; f < MVF; ++f) {
-      const int idx = tid + f * kNT;
-      mv_frag[f] = make_uint4(0, 0, 0, 0);
-      if (idx < n_frag) mv_frag[f] = ld16(tail_src(a, s, base, slot_new, B, idx));
-    }
-    __syncthreads();                                   // keys and subset sizes complete
-    // Quotas: floor(M/2) near, the rest far; a short subset gives all it has.
-    const int E = a.M;
-    const int nn = es.cnt[0], nf = es.cnt[1];
-    int qn = E / 2, qf = E - qn;
-    if (nn < qn) {
-      qn = nn;
-      qf = E - qn;
-    } else if (nf < qf) {
-      qf = nf;
-      qn = E - qf;
-    }
-    const bool sel_ok = qn <= nn && qf <= nf;
-    // Rank of each candidate inside its subset (keys of one subset form one
-    // key range); evicted iff rank < quota.
-    if (sel_ok) {
-      for (int j = tid; j < c; j += kNT) {
-        const uint64_t kj = keys[j];
-        const int sb = skey_sub(kj);
-        const uint64_t lo = uint64_t(sb & 1) << 62;
-        int r = 0;
-        int i = 0;
-        for (; i + 8 <= c; i += 8) {
-          uint64_t kk[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) kk[u] = keys[i + u];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) r += (kk[u] >= lo) & (kk[u] < kj);
-        }
-        for (; i < c; ++i) {
-          const uint64_t ki = keys[i];
-          r += (ki >= lo) & (ki < kj);
-        }
-        evf[j] = (sb < 2 && r < (sb == 0 ? qn : qf)) ? 1 : 0;
-      }
-    }
-    if (!sel_ok) {
-      if (tid == 0) atomicOr(a.err, HKV_ERRBIT_SELECT);
-      if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
-    } else {
-      __syncthreads();
-      if (wave == 0) {
-        int nh = 0, nm = 0, ne = 0;
-        const uint64_t lt = lanemask_lt(lane);
-        for (int j0 = 0; j0 < c; j0 += kWave) {
-          const int j = j0 + lane;
-          const bool in = j < c;
-          const bool ev = in && evf[j];
-          const bool hole = ev && j < B;
-          const bool mover = in && !ev && j >= B;
-          const uint64_t mh = __ballot(hole), mm = __ballot(mover), me = __ballot(ev);
-          if (hole) {
-            const int r = nh + __popcll(mh & lt);
-            if (r < kMaxEvict) es.holes[r] = j;
-          }
-          if (mover) {
-            const int r = nm + __popcll(mm & lt);
-            if (r < kMaxEvict) es.movers[r] = j;
-          }
-          if (j >= B && j < B + a.M) es.mover_rank[j - B] = mover ? nm + __popcll(mm & lt) : -1;
-          if (ev && a.log) {
-            const int r = ne + __popcll(me & lt);
-            if (r < a.M) a.log[(long long)s * a.M + r] = skey_pos(keys[j]);
-          }
-          nh += __popcll(mh);
-          nm += __popcll(mm);
-          ne += __popcll(me);
-        }
-        if (lane == 0) {
-          es.nh = nh;
-          es.nm = nm;
-          es.ne = ne;
-        }
-        if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
-      }
-      __syncthreads();
-      const int nmv = es.nh;
-      if (es.nh != es.nm || es.ne != a.M || es.nh > kMaxEvict) {
-        if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
-      } else {
-        // K/V rows of the movers into the holes (tail fill), mostly from the
-        // fragments fetched before the selection
-        for (int idx = tid, f = 0; idx < n_frag; idx += kNT, ++f) {
-          const int k = es.mover_rank[idx / (2 * G)];
-          if (k < 0) continue;
-          uint4 v;
-          if (f < MVF) {
-#pragma unroll
-            for (int ff = 0; ff < MVF; ++ff)
-              if (ff == f) v = mv_frag[ff];
-          } else {
-            v = ld16(tail_src(a, s, base, slot_new, B, idx));
-          }
-          const bool isv = (idx % (2 * G)) >= G;
-          st16((isv ? a.v_pool : a.k_pool) + ((base + es.holes[k]) * D + (idx % G) * VE) * ES, v);
-        }
-        if (tid < nmv) {
-          const uint64_t mk = keys[es.movers[tid]];
-          a.pos[base + es.holes[tid]] = skey_pos(mk);
-          a.score[base + es.holes[tid]] = skey_score(mk);
-        }
-        if (AT) {   // deferred score writes of the kept slots below the budget
-          for (int j = tid; j < B; j += kNT)
-            if (!evf[j]) a.score[base + j] = skey_score(keys[j]);
-        }
-        c_final = B;
-      }
-    }
-  } else if (EV && a.log && tid < a.M) {
-    a.log[(long long)s * a.M + tid] = -1;
-  }
-
-  if (tid == 0 && (AP || c_final != c)) a.count[s] = c_final;
-}
-
-// ------------------------------------------------------------------ k_step
-// One workgroup per stream.  Every thread reads the stream's metadata itself
-// (uniform loads, no barrier); the query, the score window and the positions
-// needed by an eviction are requested together with the first K/V rows.
-template <class T, int D, bool AP, bool AT, bool EV>
-__global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
-  using F = Frag<T>;
-  constexpr int VE = F::N;           // elements per 16-byte fragment
-  constexpr int G = D / VE;          // lanes per row
-  constexpr int R = kWave / G;       // rows per wave instruction
-  constexpr int U = HKV_U;           // row fragments in flight per lane
-  constexpr int ES = sizeof(T);
-  constexpr int KPT = HKV_KPT;       // prefetched score slots per thread
-
-  __shared__ CombineShared cs;
-  __shared__ EvictShared es;
-  __shared__ float lds_lg[AT ? kLdsSlots : 1];
-  __shared__ uint64_t lds_key[EV ? kLdsSlots : 1];
-  __shared__ uint8_t lds_evf[EV ? kLdsSlots : 1];
-  (void)R; (void)U; (void)KPT;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = a.s_begin + blockIdx.x;
-  const int g = lane / G, sub = lane % G;
-  if (EV && tid < 2) es.cnt[tid] = 0;
-
-  // query fragment first: its address does not depend on the stream metadata
-  uint4 q_raw = make_uint4(0, 0, 0, 0);
-  if (AT) q_raw = ld16(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
-
-  // the label byte through the scalar path (aligned 32-bit word), except in a
-  // last partial word
-  int lab;
-  if (4LL * ((s >> 2) + 1) <= a.S)
-    lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
-  else
-    lab = a.label[s];
-  const int c0 = a.count[s];
-  const int capv = a.cap[s];
-  const int B = a.budget[s];
-  const long long base = a.base[s];
-  const bool glob = lab == HKV_GLOBAL;
-  int c = c0, slot_new = -1;
-  bool ok = true;
-  if (AP) {
-    if (lab == HKV_LOCAL) {
-      slot_new = a.t % a.w;
-      c = c0 + 1 < a.w ? c0 + 1 : a.w;
-    } else {
-      slot_new = c0;
-      c = c0 + 1;
-      if (c0 >= capv) {
-        ok = false;
-        if (tid == 0) atomicOr(a.err, HKV_ERRBIT_CAPACITY);
-      }
+  int nf_final = nf;
+  if (EV) {
+    if (due) {
+      const bool ready = tile_here;
+      if (onchip)
+        nf_final = evict_stream<T, D, AP>(a, x, scr_l, es, ready);
+      else
+        nf_final = evict_stream<T, D, AP>(a, x, scr_g, es, ready);
+    } else if (a.log && tid < a.M) {
+      a.log[(long long)s * a.M + tid] = -1;
     }
   }
-  if (ok && (c < 1 || c > capv || lab > HKV_FULL)) {
-    ok = false;
-    if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
-  }
-  if (!ok) {
-    if (EV && a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
-    return;
-  }
-  const bool write_mode = glob && (c == B + a.M - a.W + 1);
-  const bool due = EV && glob && (c == B + a.M);
 
-  StepCtx x;
-  x.base = base;
-  x.s = s;
-  x.lab = lab;
-  x.c = c;
-  x.B = B;
-  x.slot_new = slot_new;
-  x.glob = glob;
-  x.write_mode = write_mode;
-  x.due = due;
-  (void)lane; (void)wave; (void)g;
-  if (c <= kLdsSlots)
-    step_body<T, D, AP, AT, EV>(a, x, q_raw, lds_lg, lds_key, lds_evf, cs, es);
-  else
-    step_body<T, D, AP, AT, EV>(a, x, q_raw, a.ws_logits + base, a.ws_keys + base,
-                                reinterpret_cast<uint8_t*>(a.ws_logits + base), cs, es);
+  if (tid == 0) {
+    if (AP) a.count[s] = ext;
+    if (glob && nf_final != nf0) a.n_free[s] = nf_final;
+  }
 }
 
 // ------------------------------------------------------------------ k_classify
@@ -636,6 +834,7 @@ struct LayoutArgs {
   char* k_pool; char* v_pool;
   int* pos; float* score;
   long long* base; int* cap; int* count; int* budget; int* n_tokens; unsigned char* label;
+  int* n_free;
   int* err;
   int H, N, P, w, W, M, D, A, full;
   long long group_slots;
@@ -690,6 +889,7 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
     a.base[s] = s_base;
     a.budget[s] = s_B;
     a.count[s] = s_count;
+    a.n_free[s] = 0;
   }
   __syncthreads();
   const long long base = s_base;
@@ -781,6 +981,7 @@ float scale_log2_of(int d) { return float(1.4426950408889634 / std::sqrt(double(
 
 dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, int t) {
   dev::StepArgs a{};
+  char* ws = static_cast<char*>(st->workspace);
   a.k_pool = static_cast<char*>(st->k_pool);
   a.v_pool = static_cast<char*>(st->v_pool);
   a.pos = st->pos;
@@ -790,9 +991,13 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.budget = st->budget;
   a.cap = st->cap;
   a.label = st->label;
+  a.free_slots = st->free_slots;
+  a.n_free = st->n_free;
   a.err = st->err;
-  a.ws_logits = reinterpret_cast<float*>(static_cast<char*>(st->workspace) + d.ws_logits);
-  a.ws_keys = reinterpret_cast<uint64_t*>(static_cast<char*>(st->workspace) + d.ws_keys);
+  a.ws_tile = reinterpret_cast<float*>(ws + d.ws_tile);
+  a.ws_pos = reinterpret_cast<int*>(ws + d.ws_pos);
+  a.ws_keys = reinterpret_cast<uint64_t*>(ws + d.ws_keys);
+  a.ws_evf = reinterpret_cast<uint8_t*>(ws + d.ws_evf);
   a.t = t;
   a.w = c->local_window;
   a.W = c->w_obs;
@@ -892,6 +1097,7 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
   b.budget = st->budget;
   b.n_tokens = st->n_tokens;
   b.label = st->label;
+  b.n_free = st->n_free;
   b.err = st->err;
   b.H = c->heads;
   b.N = c->final_len;
@@ -961,15 +1167,23 @@ hkv_status hkv_decode_attn(const hkv_config* c, hkv_state* st, int32_t t, const 
   return after_launch("k_step(attn)");
 }
 
-hkv_status hkv_ste_evict(const hkv_config* c, hkv_state* st, int32_t t, int32_t* log,
-                         int32_t s_begin, int32_t s_count, void* stream) {
+hkv_status hkv_ste_evict(const hkv_config* c, hkv_state* st, int32_t t, const void* q_win,
+                         int64_t ld_qw, int32_t* log, int32_t s_begin, int32_t s_count,
+                         void* stream) {
   Derived d;
   hkv_status r = common_checks(c, st, t, s_begin, s_count, &d);
   if (r != HKV_OK) return r;
+  if (q_win) {
+    if ((r = check_data_ptr(q_win, ld_qw, elem_bytes(c), "q_win")) != HKV_OK) return r;
+    if (ld_qw < int64_t(c->w_obs) * c->head_dim)
+      return fail(HKV_E_INVAL, "ld_qw smaller than w_obs * head_dim");
+  }
   if (log && (reinterpret_cast<uintptr_t>(log) & 3u))
     return fail(HKV_E_INVAL, "evicted_pos_log misaligned");
   if (s_count == 0) return HKV_OK;
   dev::StepArgs a = step_args(c, st, d, t);
+  a.q_win = static_cast<const char*>(q_win);
+  a.ld_qw = ld_qw;
   a.log = log;
   a.s_begin = s_begin;
   launch_step<false, false, true>(c, a, s_count, static_cast<hipStream_t>(stream));
@@ -977,7 +1191,7 @@ hkv_status hkv_ste_evict(const hkv_config* c, hkv_state* st, int32_t t, int32_t*
 }
 
 hkv_status hkv_decode_step(const hkv_config* c, hkv_state* st, int32_t t, const void* k_new,
-                           const void* v_new, int64_t ld_kv, const void* q, int64_t ld_q,
+                           const void* v_new, int64_t ld_kv, const void* q_win, int64_t ld_qw,
                            void* out, int64_t ld_o, int32_t* log, int32_t s_begin,
                            int32_t s_count, void* stream) {
   Derived d;
@@ -986,7 +1200,9 @@ hkv_status hkv_decode_step(const hkv_config* c, hkv_state* st, int32_t t, const 
   const int eb = elem_bytes(c);
   if ((r = check_data_ptr(k_new, ld_kv, eb, "k_new")) != HKV_OK) return r;
   if ((r = check_data_ptr(v_new, ld_kv, eb, "v_new")) != HKV_OK) return r;
-  if ((r = check_data_ptr(q, ld_q, eb, "q")) != HKV_OK) return r;
+  if ((r = check_data_ptr(q_win, ld_qw, eb, "q_win")) != HKV_OK) return r;
+  if (ld_qw < int64_t(c->w_obs) * c->head_dim)
+    return fail(HKV_E_INVAL, "ld_qw smaller than w_obs * head_dim");
   if (!out) return fail(HKV_E_INVAL, "out is NULL");
   if ((reinterpret_cast<uintptr_t>(out) & 3u) || ld_o < c->head_dim)
     return fail(HKV_E_INVAL, "out misaligned or ld_o < head_dim");
@@ -997,8 +1213,10 @@ hkv_status hkv_decode_step(const hkv_config* c, hkv_state* st, int32_t t, const 
   a.k_new = static_cast<const char*>(k_new);
   a.v_new = static_cast<const char*>(v_new);
   a.ld_kv = ld_kv;
-  a.q = static_cast<const char*>(q);
-  a.ld_q = ld_q;
+  a.q_win = static_cast<const char*>(q_win);
+  a.ld_qw = ld_qw;
+  a.q = a.q_win + (long long)(c->w_obs - 1) * c->head_dim * eb;   // newest query of the window
+  a.ld_q = ld_qw;
   a.out = static_cast<char*>(out);
   a.ld_o = ld_o;
   a.log = log;

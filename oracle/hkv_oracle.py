@@ -30,13 +30,13 @@ carry the same text) by section:
 Where the pages leave a step open, the reading used here is stated at the
 function.  The readings are the project's, not the pages'.
 
-Parity-pinned by tests/test_oracle_pins.py and tests/test_oracle_bruteforce.py
-(closed forms, invariants, textbook special cases, brute force).  The following
-are spec choices the pages do not fix and are therefore "parity unpinned" as to
+Parity-pinned by tests/test_oracle_pins.py (closed forms, invariants, textbook
+special cases, brute force, hand-worked golden examples).  The following are
+spec choices the pages do not fix and are therefore "parity unpinned" as to
 their definition (only their internal consistency is pinned): the score formula
 (sum of the last W softmax probabilities), M = W, the Global budget split, the
 protected zone of the W newest tokens, the (score, position) tie-break and the
-tail-fill slot layout.
+slot layout (evicted slots are freed and refilled by the next tokens).
 """
 from __future__ import annotations
 
@@ -131,21 +131,25 @@ def ste_select(slot_pos, slot_score, t: int, w_obs: int, split: int, n_evict: in
     return sorted(chosen)
 
 
-def tail_fill(slot_pos, slot_score, evicted: List[int], keep: int):
+def free_evicted(slot_pos, slot_score, evicted: List[int]):
     """Slot layout after an eviction (reading; the pages fix no layout): the
-    evicted slots below `keep` are refilled, in ascending order, by the
-    surviving slots at or above `keep`, in ascending order; the table is then
-    cut to `keep` slots."""
-    ev = set(evicted)
-    holes = [j for j in range(keep) if j in ev]
-    movers = [j for j in range(keep, len(slot_pos)) if j not in ev]
-    assert len(holes) == len(movers)
-    pos = list(slot_pos[:keep])
-    sc = list(slot_score[:keep])
-    for h, m in zip(holes, movers):
-        pos[h] = slot_pos[m]
-        sc[h] = slot_score[m]
-    return pos, sc
+    evicted slots become free (position -1, score 0); no other slot moves.
+    Returns the new table, the new scores and the free slots, ascending."""
+    pos = list(slot_pos)
+    sc = list(slot_score)
+    for j in evicted:
+        pos[j] = -1
+        sc[j] = 0.0
+    return pos, sc, sorted(evicted)
+
+
+def append_slot(table: List[int], free: List[int]) -> int:
+    """Slot receiving the next token of a Global stream (reading): the lowest
+    free slot if any, else a new slot at the end of the table."""
+    if free:
+        return free.pop(0)
+    table.append(-1)
+    return len(table) - 1
 
 
 def scoring_window_starts(count: int, budget: int, n_evict: int, w_obs: int) -> bool:
@@ -273,6 +277,7 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
     rec.tables_after_classify = [list(t) for t in tables]
 
     # ---- decode steps [Method/3L], [Method/3G] ----
+    free: List[List[int]] = [[] for _ in range(H)]
     out = np.zeros((H, T, d))
     for step in range(T):
         t = P + step
@@ -281,21 +286,26 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
             lab = labels[h]
             if lab == LOCAL:
                 tables[h][t % w] = t
-                present = [pos for pos in tables[h] if pos >= 0]
-            else:
+            elif lab == FULL:
                 tables[h].append(t)
-                scores[h].append(0.0)
-                present = tables[h]
-            pos_arr = np.array(present, dtype=np.int64)
+            else:
+                j = append_slot(tables[h], free[h])
+                if j == len(scores[h]):
+                    scores[h].append(0.0)
+                tables[h][j] = t
+                scores[h][j] = 0.0
+            live = [j for j, pos in enumerate(tables[h]) if pos >= 0]
+            pos_arr = np.array([tables[h][j] for j in live], dtype=np.int64)
             o, p = attend(q, K[h, pos_arr], V[h, pos_arr])
             out[h, step] = o
             if lab != GLOBAL:
                 continue
-            c = len(tables[h])
+            c = len(live)
             if scoring_window_starts(c, B, M, W):
-                scores[h] = [float(x) for x in p]
-            else:
-                scores[h] = [float(a) + float(b) for a, b in zip(scores[h], p)]
+                for j in live:
+                    scores[h][j] = 0.0
+            for j, pj in zip(live, p):
+                scores[h][j] = float(scores[h][j]) + float(pj)
             if c == B + M:
                 own = ste_select(tables[h], scores[h], t, W, D, M)
                 use = own
@@ -304,7 +314,7 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
                     if alt is not None:
                         use = sorted(alt)
                 rec.events.append(Event(h, t, list(tables[h]), list(scores[h]), use, own, B))
-                tables[h], scores[h] = tail_fill(tables[h], scores[h], use, B)
+                tables[h], scores[h], free[h] = free_evicted(tables[h], scores[h], use)
     rec.outputs = out
     rec.tables_final = [list(t) for t in tables]
     return rec

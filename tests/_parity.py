@@ -95,13 +95,14 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
         t = P + step
         kp = K.data_ptr() + t * d * eb
         vp = V.data_ptr() + t * d * eb
-        qp = Q.data_ptr() + (t - (P - W)) * d * eb
+        qp = Q.data_ptr() + (t - (P - W)) * d * eb          # query of position t
+        qw = Q.data_ptr() + (t - W + 1 - (P - W)) * d * eb  # positions t-W+1 .. t
         if mode == "fused":
-            hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qp, w.q_rows * d, out, d, log, 0, S)
+            hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log, 0, S)
         else:
             hk.hkv_append(cfg, st, t, kp, vp, N * d, 0, S)
             hk.hkv_decode_attn(cfg, st, t, qp, w.q_rows * d, out, d, 0, S)
-            hk.hkv_ste_evict(cfg, st, t, log, 0, S)
+            hk.hkv_ste_evict(cfg, st, t, qw, w.q_rows * d, log, 0, S)
         outs[step] = out[idx]
         logs[step] = log[idx]
     hk.hkv_check(cfg, st)
@@ -124,6 +125,7 @@ class Report:
     events_checked: int = 0
     outputs_checked: int = 0
     max_out_err: float = 0.0
+    max_score_err: float = 0.0
 
     def fail(self, msg: str):
         if len(self.failures) < 50:
@@ -228,6 +230,17 @@ def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
             tf = [p for p in tf[:int(g.count_final[c])]]
         if tf != g.tables_final[c]:
             rep.fail(f"l{l} b{b} h{h}: final layout differs")
+        # scores written at the stream's last eviction (0 for freed slots; slots
+        # refilled after it were reset to 0 by their append)
+        evs = [ev for ev in rec.events if ev.head == h]
+        if evs and lab == O.GLOBAL:
+            ev = evs[-1]
+            _, want, _ = O.free_evicted(ev.slot_pos, ev.slot_score, ev.evicted_slots)
+            got_sc = np.asarray(g.scores_final[c][:len(want)], dtype=np.float64)
+            err = float(np.max(np.abs(got_sc - np.asarray(want)))) if len(want) else 0.0
+            rep.max_score_err = max(rep.max_score_err, err)
+            if err > EPS_S:
+                rep.fail(f"l{l} b{b} h{h}: scores at the last eviction differ by {err:.3g}")
         ref = rec.outputs[h]
         got = g.outs[:T, c]
         if w.dtype == "bf16":

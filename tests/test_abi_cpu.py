@@ -59,6 +59,7 @@ def test_validate_workloads_and_sizes():
     (dict(rho=(5, 4)), hk.E_INVAL),
     (dict(rho=(1, 100)), hk.E_INVAL),      # floor(rho N) < w
     (dict(evict_m=7, w_obs=7), hk.E_INVAL),
+    (dict(evict_m=10, w_obs=10), hk.E_INVAL),  # window longer than 8
     (dict(evict_m=6), hk.E_UNSUPPORTED),   # M != W
     (dict(split_dist=4), hk.E_INVAL),
     (dict(prefill_len=2000, final_len=3000), hk.E_UNSUPPORTED),
@@ -76,7 +77,7 @@ def _fake_state(cfg, phase=1):
     """A state whose pointers are aligned but never dereferenced: every call
     below fails its host checks before anything is enqueued."""
     a = 1 << 20
-    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg), phase)
+    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg), phase)
     return st
 
 
@@ -98,8 +99,11 @@ def test_entry_points_reject_before_launch():
         (lambda: hk.hkv_append(cfg, st, 40, buf, buf, 64, -1, 1), hk.E_INVAL),
         (lambda: hk.hkv_decode_attn(cfg, st, 40, buf, 64, None, 64, 0, 16), hk.E_INVAL),
         (lambda: hk.hkv_decode_attn(cfg, st, 40, buf, 64, buf, 32, 0, 16), hk.E_INVAL),
-        (lambda: hk.hkv_ste_evict(cfg, st, 40, buf + 2, 0, 16), hk.E_INVAL),
-        (lambda: hk.hkv_decode_step(cfg, st, 40, buf, buf, 64, buf, 64, buf, 64, None, 0, 17),
+        (lambda: hk.hkv_ste_evict(cfg, st, 40, None, 0, buf + 2, 0, 16), hk.E_INVAL),
+        (lambda: hk.hkv_ste_evict(cfg, st, 40, buf, 64, None, 0, 16), hk.E_INVAL),   # ld_qw < W*d
+        (lambda: hk.hkv_decode_step(cfg, st, 40, buf, buf, 64, buf, 512, buf, 64, None, 0, 17),
+         hk.E_INVAL),
+        (lambda: hk.hkv_decode_step(cfg, st, 40, buf, buf, 64, None, 512, buf, 64, None, 0, 16),
          hk.E_INVAL),
         (lambda: hk.hkv_classify(cfg, st, None, buf, 40 * 64, buf, 512), hk.E_INVAL),
         (lambda: hk.hkv_classify(cfg, st, buf, buf, 10, buf, 512), hk.E_INVAL),
@@ -109,7 +113,7 @@ def test_entry_points_reject_before_launch():
         with pytest.raises(hk.HkvError) as e:
             fn()
         assert e.value.status == code, (i, hk.hkv_last_error())
-    bad = hk.hkv_state(*([0] * 12), 0, 1)
+    bad = hk.hkv_state(*([0] * 14), 0, 1)
     with pytest.raises(hk.HkvError) as e:
         hk.hkv_append(cfg, bad, 40, buf, buf, 64, 0, 16)
     assert e.value.status == hk.E_INVAL

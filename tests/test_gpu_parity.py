@@ -61,7 +61,8 @@ def test_parity_small(name):
     for (l, b) in groups:
         rep = oracle_check_group(w, 0, l, b, g, rep=rep)
     print(f"  outputs {rep.outputs_checked} events {rep.events_checked} "
-          f"max err {rep.max_out_err:.3g} flags {rep.flagged_counts}/{rep.flagged_labels}/"
+          f"max err {rep.max_out_err:.3g} score err {rep.max_score_err:.3g} "
+          f"flags {rep.flagged_counts}/{rep.flagged_labels}/"
           f"{rep.flagged_evictions}", flush=True)
     assert not rep.failures, rep.failures[:8]
     if name not in ("rho_one", "full_cache", "wide_window"):
@@ -144,20 +145,24 @@ def test_evict_given_identical_scores(dtype, d):
         cache.v_pool[base:base + c] = torch.from_numpy(V[s][pos]).to(dt).cuda()
         cache.state.phase = 1
         log = torch.full((w.S, w.evict_m), -7, dtype=torch.int32, device="cuda")
-        hk.hkv_ste_evict(cfg, cache.state, ev.t, log, s, 1)
+        hk.hkv_ste_evict(cfg, cache.state, ev.t, None, 0, log, s, 1)
         hk.hkv_check(cfg, cache.state)
         own = O.ste_select(ev.slot_pos, sc32.astype(np.float64), ev.t, w.w_obs, w.split_dist,
                            w.evict_m)
-        want_pos, _ = O.tail_fill(ev.slot_pos, list(sc32), own, ev.budget)
+        want_pos, want_sc, want_free = O.free_evicted(ev.slot_pos, list(sc32), own)
         got_log = log[s].cpu().numpy()
-        assert sorted(got_log.tolist()) == sorted(ev.slot_pos[j] for j in own)
-        assert int(cache.count[s]) == ev.budget
-        got_pos = cache.pos[base:base + ev.budget].cpu().numpy().tolist()
+        assert got_log.tolist() == [ev.slot_pos[j] for j in own]       # ascending slots
+        assert int(cache.count[s]) == c                                  # no row moves
+        assert int(cache.n_free[s]) == w.evict_m
+        assert cache.free_slots[s].cpu().numpy().tolist() == want_free
+        got_pos = cache.pos[base:base + c].cpu().numpy().tolist()
         assert got_pos == want_pos
-        got_k = cache.k_pool[base:base + ev.budget].float().cpu().numpy()
-        assert np.array_equal(got_k, K[s][want_pos].astype(np.float32)
-                              if dtype == "f32" else
-                              torch.from_numpy(K[s][want_pos]).to(dt).float().numpy())
+        got_sc = cache.score[base:base + c].cpu().numpy()
+        assert np.array_equal(got_sc, np.array(want_sc, dtype=np.float32))
+        kept = [j for j in range(c) if j not in set(own)]
+        got_k = cache.k_pool[base:base + c].float().cpu().numpy()[kept]
+        want_k = torch.from_numpy(K[s][pos[kept]]).to(dt).float().numpy()
+        assert np.array_equal(got_k, want_k)
 
 
 def test_capacity_error_reported():

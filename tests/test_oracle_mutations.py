@@ -72,14 +72,18 @@ def _select_newest_first_on_ties(slot_pos, slot_score, t, w_obs, split, n_evict)
     return sorted(sorted(near, key=key)[:q_near] + sorted(far, key=key)[:q_far])
 
 
-def _tail_fill_descending(slot_pos, slot_score, evicted, keep):
-    ev = set(evicted)
-    holes = [j for j in range(keep) if j in ev]
-    movers = [j for j in range(len(slot_pos) - 1, keep - 1, -1) if j not in ev]
-    pos, sc = list(slot_pos[:keep]), list(slot_score[:keep])
-    for h, m in zip(holes, movers):
-        pos[h], sc[h] = slot_pos[m], slot_score[m]
-    return pos, sc
+def _append_highest_free(table, free):          # refills freed slots in descending order
+    if free:
+        return free.pop()
+    table.append(-1)
+    return len(table) - 1
+
+
+def _free_evicted_keep_scores(slot_pos, slot_score, evicted):   # evicted scores not cleared
+    pos = list(slot_pos)
+    for j in evicted:
+        pos[j] = -1
+    return pos, list(slot_score), sorted(evicted)
 
 
 def _budget_uniform(heads, per_head, window, n_local):
@@ -102,7 +106,8 @@ MUTANTS = {
     "select_protect_off_by_one": ("ste_select", _select_protect_off_by_one),
     "select_quota_swapped": ("ste_select", _select_quota_swapped),
     "select_newest_first_on_ties": ("ste_select", _select_newest_first_on_ties),
-    "tail_fill_descending": ("tail_fill", _tail_fill_descending),
+    "append_highest_free": ("append_slot", _append_highest_free),
+    "free_keeps_scores": ("free_evicted", _free_evicted_keep_scores),
     "budget_uniform": ("global_budget", _budget_uniform),
     "budget_ceil": ("global_budget", _budget_ceil),
     "score_window_never_reset": ("scoring_window_starts", lambda *a: False),

@@ -171,9 +171,16 @@ def check_ste_events(orc, cfg, rec):
         far_c = sum(1 for p in pos if t - p >= D)
         if near_c >= M // 2 and far_c >= M - M // 2:
             assert n_near == M // 2
-        # tail fill moves exactly the M tail slots into the M holes
-        assert all(j < ev.budget for j in ev.evicted_slots)
-        assert sorted(pos[ev.budget:]) == list(range(t - M + 1, t + 1))
+        assert -1 not in pos                    # no free slot at an eviction
+    # layout: the M tokens after an eviction fill its freed slots, ascending
+    by_head = {}
+    for ev in rec.events:
+        by_head.setdefault(ev.head, []).append(ev)
+    for evs in by_head.values():
+        for a, b in zip(evs, evs[1:]):
+            assert b.t == a.t + M
+            assert [b.slot_pos[j] for j in sorted(a.evicted_slots)] == \
+                list(range(a.t + 1, a.t + M + 1))
 
 
 def check_score_sum(orc, cfg, rec):
@@ -212,7 +219,7 @@ def check_layout(orc, cfg, rec):
         for ev in rec.init_events + rec.events:
             if ev.head == h:
                 gone |= {ev.slot_pos[j] for j in ev.evicted_slots}
-        final = rec.tables_final[h]
+        final = [p for p in rec.tables_final[h] if p >= 0]
         assert len(set(final)) == len(final)
         assert set(final) == set(range(cfg.N)) - gone
 
@@ -242,11 +249,17 @@ def check_ste_golden(orc):
         ev = orc.ste_select(pos, score, t, W, D, E)
         assert sorted(pos[j] for j in ev) == [int(x) for x in ex["evicted_pos"].split()], name
         want_after = [int(x) for x in ex["table_after"].split()]
-        if ex["mode"] == "decode":       # tail fill
-            after, _ = orc.tail_fill(pos, score, ev, keep)
+        if ex["mode"] == "decode":        # evicted slots freed, refilled ascending
+            after, sc_after, free = orc.free_evicted(pos, score, ev)
+            assert after == want_after, name
+            assert all(sc_after[j] == 0.0 for j in ev)
+            table = list(after)
+            slots = [orc.append_slot(table, free) for _ in range(E)]
+            assert slots == [int(x) for x in ex["refill"].split()], name
+            assert orc.append_slot(table, free) == len(pos), name    # then the table grows
         else:                               # classification time: order-preserving
             after = [pos[j] for j in range(len(pos)) if j not in set(ev)]
-        assert after == want_after, name
+            assert after == want_after, name
 
 
 def check_ste_bruteforce(orc, trials=200):
