@@ -80,8 +80,6 @@ hkv_status derive(const hkv_config* c, Derived* d) {
   off = align256(off + size_t(d->pool_slots) * sizeof(int32_t));
   d->ws_keys = off;
   off = align256(off + size_t(d->pool_slots) * sizeof(uint64_t));
-  d->ws_evf = off;
-  off = align256(off + size_t(d->pool_slots));
   d->ws_bytes = off;
   return HKV_OK;
 }

@@ -26,7 +26,6 @@ struct Derived {
   size_t ws_tile = 0;          // float [pool_slots * w_obs]
   size_t ws_pos = 0;           // int32 [pool_slots]
   size_t ws_keys = 0;          // uint64 [pool_slots]
-  size_t ws_evf = 0;           // uint8 [pool_slots]
   size_t ws_bytes = 0;
 };
 

@@ -28,7 +28,7 @@ namespace hkv {
 namespace dev {
 
 // Tuning knobs (compile-time): waves per workgroup, row fragments in flight per
-// lane, minimum waves per SIMD.
+// lane, key tiles in flight per wave on the matrix-core path.
 #ifndef HKV_NW
 #define HKV_NW 4
 #endif
@@ -38,8 +38,17 @@ namespace dev {
 #ifndef HKV_UT
 #define HKV_UT 1
 #endif
-#ifndef HKV_WPE
-#define HKV_WPE 1
+// Occupancy the compiler schedules the decode step for (waves per SIMD): it
+// bounds the registers and so decides how many loads the hot loop keeps in
+// flight per wave versus how many waves overlap.  Measured on MI355X.
+#ifndef HKV_WPE_B64
+#define HKV_WPE_B64 6
+#endif
+#ifndef HKV_WPE_B128
+#define HKV_WPE_B128 4
+#endif
+#ifndef HKV_WPE_F32
+#define HKV_WPE_F32 4
 #endif
 constexpr int kNW = HKV_NW;            // waves per workgroup
 constexpr int kNT = kNW * kWave;
@@ -56,7 +65,7 @@ struct StepArgs {
   const unsigned char* label;
   int* free_slots; int* n_free;
   int* err;
-  float* ws_tile; int* ws_pos; uint64_t* ws_keys; uint8_t* ws_evf;   // per-slot spill
+  float* ws_tile; int* ws_pos; uint64_t* ws_keys;   // per-slot spill
   int s_begin, t, w, W, M, D;
   int S;                               // streams in the state (label array length)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
@@ -66,6 +75,7 @@ struct CombineShared {
   float m[kNW];
   float l[kNW];
   float o[kNW][128];
+  float wm[kNW][kMaxWobs], wl[kNW][kMaxWobs];   // window-query softmax partials
 };
 
 struct EvictShared {
@@ -92,14 +102,13 @@ struct StepCtx {
 };
 
 // Per-slot scratch of an eviction: the W x c score tile (aliased by the keys
-// once the scores are formed), positions and eviction flags.  On chip (LDS)
+// once the scores are formed) and the positions (reused as rank counters).  On chip (LDS)
 // for streams of at most kLdsSlots slots, else in the workspace; instantiating
 // both cases lets the compiler address the on-chip case with LDS instructions.
 struct Scratch {
   float* tile;
-  int* pos;
+  int* pos;                            // positions, then rank counters
   uint64_t* keys;
-  uint8_t* evf;
 };
 
 // ------------------------------------------------------------------ eviction
@@ -208,7 +217,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       }
     }
   }
-  if (window) {
+  if (window && !tile_ready) {
     __syncthreads();
     // softmax statistics of each window query over the slots it sees
     for (int i = wave; i < W; i += kNW) {
@@ -226,59 +235,72 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         es.ql[i] = l;
       }
     }
-    __syncthreads();
-  } else {
-    __syncthreads();
   }
+  __syncthreads();              // tile, positions and window statistics complete
 
-  // scores -> keys (the keys overwrite the tile: read first, then write)
+  // scores of the slots; the keys overwrite the tile, so read it first.  Each
+  // slot's position entry becomes its rank counter (read first by its owner).
   constexpr int SPT = (kLdsSlots + kNT - 1) / kNT;
   float scv[SPT];
+  int pjv[SPT];
   int nn = 0, nf = 0;
-  for (int k = 0, j = tid; k < SPT || j < c; ++k, j += kNT) {
-    if (j >= c) break;
+  auto score_of = [&](int j, int pj) {
     float v = 0.f;
     if (window) {
-      const int pj = sc.pos[j];
       for (int i = 0; i < W; ++i)
         if (pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * (1.0f / es.ql[i]);
     } else {
       v = (AP && j == slot_new) ? 0.0f : a.score[base + j];
     }
-    if (k < SPT) {
-#pragma unroll
-      for (int kk = 0; kk < SPT; ++kk)
-        if (kk == k) scv[kk] = v;
-    } else {
-      // streams beyond the on-chip size keep keys apart from the tile
-      const int pj = sc.pos[j];
-      const int dist = t - pj;
-      const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
-      nn += sb == 0;
-      nf += sb == 1;
-      sc.keys[j] = make_skey(sb, v, pj);
-    }
-  }
-  __syncthreads();
+    return v;
+  };
+  auto sub_of = [&](int pj) {
+    const int dist = t - pj;
+    return dist < W ? 2 : (dist < Dd ? 0 : 1);
+  };
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int j = tid + k * kNT;
+    scv[k] = 0.f;
+    pjv[k] = 0;
     if (j < c) {
-      const int pj = sc.pos[j];
-      const int dist = t - pj;
-      const int sb = dist < W ? 2 : (dist < Dd ? 0 : 1);
-      nn += sb == 0;
-      nf += sb == 1;
-      sc.keys[j] = make_skey(sb, scv[k], pj);
+      pjv[k] = sc.pos[j];
+      scv[k] = score_of(j, pjv[k]);
     }
   }
-  nn = wave_sum_int(nn);
-  nf = wave_sum_int(nf);
+  for (int j = tid + SPT * kNT; j < c; j += kNT) {    // beyond the on-chip size: keys apart
+    const int pj = sc.pos[j];
+    const int sb = sub_of(pj);
+    nn += sb == 0;
+    nf += sb == 1;
+    sc.keys[j] = make_skey(sb, score_of(j, pj), pj);
+    sc.pos[j] = 0;
+  }
+  __syncthreads();              // tile consumed
+#pragma unroll
+  for (int k = 0; k < SPT; ++k) {
+    const int j = tid + k * kNT;
+    const int sb = sub_of(pjv[k]);
+    const bool in = j < c;
+    if (in) {
+      sc.keys[j] = make_skey(sb, scv[k], pjv[k]);
+      sc.pos[j] = 0;
+    }
+    const uint64_t m0 = __ballot(in && sb == 0), m1 = __ballot(in && sb == 1);
+    if (lane == 0) {
+      nn += __popcll(m0);
+      nf += __popcll(m1);
+    }
+  }
+  if (c > SPT * kNT) {
+    nn = wave_sum_int(nn);
+    nf = wave_sum_int(nf);
+  }
   if (lane == 0) {
     if (nn) atomicAdd(&es.cnt[0], nn);
     if (nf) atomicAdd(&es.cnt[1], nf);
   }
-  __syncthreads();
+  __syncthreads();              // keys, subset sizes, zeroed rank counters
 
   // quotas: floor(M/2) near, the rest far; a short subset gives all it has
   const int E = a.M;
@@ -296,33 +318,44 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
     return 0;
   }
-  // rank of each candidate inside its subset (one key range per subset)
-  for (int j = tid; j < c; j += kNT) {
+  // rank of each candidate inside its subset (one key range per subset): P
+  // threads per slot, each counting over a share of the keys
+  const int P = c <= kNT ? kNT / c : 1;
+  const int len = (c + P - 1) / P;
+  for (int idx = tid; idx < c * P; idx += kNT) {
+    const int j = idx % c, part = idx / c;
     const uint64_t kj = sc.keys[j];
     const int sb = skey_sub(kj);
-    const uint64_t lo = uint64_t(sb & 1) << 62;
-    int r = 0, i = 0;
-    for (; i + 8 <= c; i += 8) {
+    if (sb >= 2) continue;
+    const uint64_t lo = uint64_t(sb) << 62;
+    const int i0 = part * len, i1 = min(c, i0 + len);
+    int r = 0, i = i0;
+    for (; i + 8 <= i1; i += 8) {
       uint64_t kk[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) kk[u] = sc.keys[i + u];
 #pragma unroll
       for (int u = 0; u < 8; ++u) r += (kk[u] >= lo) & (kk[u] < kj);
     }
-    for (; i < c; ++i) {
+    for (; i < i1; ++i) {
       const uint64_t ki = sc.keys[i];
       r += (ki >= lo) & (ki < kj);
     }
-    sc.evf[j] = (sb < 2 && r < (sb == 0 ? qn : qf)) ? 1 : 0;
+    if (r) atomicAdd(&sc.pos[j], r);
   }
   __syncthreads();
+  auto evicted = [&](int j) {
+    const uint64_t kj = sc.keys[j];
+    const int sb = skey_sub(kj);
+    return sb < 2 && sc.pos[j] < (sb == 0 ? qn : qf);
+  };
   // the evicted slots, ascending: free list, log, positions
   if (wave == 0) {
     int ne = 0;
     const uint64_t lt = lanemask_lt(lane);
     for (int j0 = 0; j0 < c; j0 += kWave) {
       const int j = j0 + lane;
-      const bool ev = j < c && sc.evf[j];
+      const bool ev = j < c && evicted(j);
       const uint64_t me = __ballot(ev);
       if (ev) {
         const int r = ne + __popcll(me & lt);
@@ -339,7 +372,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   }
   // with a log, the scores of the event (0 for the freed slots)
   if (a.log)
-    for (int j = tid; j < c; j += kNT) a.score[base + j] = sc.evf[j] ? 0.0f : skey_score(sc.keys[j]);
+    for (int j = tid; j < c; j += kNT) a.score[base + j] = evicted(j) ? 0.0f : skey_score(sc.keys[j]);
   __syncthreads();
   if (es.ne != a.M) {
     if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
@@ -397,6 +430,8 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
   for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[kc][e] = 0.f;
+  // online softmax statistics of the window queries held in rows r < 3
+  float wm[3] = {kNeg, kNeg, kNeg}, wl[3] = {0.f, 0.f, 0.f};
 
   for (int tt = t0; tt < t1; tt += UT) {
     uint4 kb[UT][KC], vb[UT][KC];
@@ -405,16 +440,24 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
     for (int u = 0; u < UT; ++u) {
       const int j = (tt + u) * 16 + li;
       const bool valid = (tt + u < t1) && j < c;
-      const bool fresh = AP && j == slot_new;
-      const char* kr = fresh ? knew : a.k_pool + (base + j) * D * ES;
-      const char* vr = fresh ? vnew : a.v_pool + (base + j) * D * ES;
+      const int jj = valid ? j : 0;              // branch-free: clamp, then zero
+      const bool fresh = AP && jj == slot_new;
+      const char* kr = fresh ? knew : a.k_pool + (base + jj) * D * ES;
+      const char* vr = fresh ? vnew : a.v_pool + (base + jj) * D * ES;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        kb[u][kc] = valid ? ld16(kr + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
-        vb[u][kc] = valid ? ld16(vr + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
+        kb[u][kc] = ld16(kr + (lk * 8 + kc * 32) * ES);
+        vb[u][kc] = ld16(vr + (lk * 8 + kc * 32) * ES);
       }
       pv[u] = 0;
-      if (due && lk == 0 && valid) pv[u] = fresh ? a.t : a.pos[base + j];
+      if (due) pv[u] = fresh ? a.t : a.pos[base + jj];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (!valid) {
+          kb[u][kc] = make_uint4(0, 0, 0, 0);
+          vb[u][kc] = make_uint4(0, 0, 0, 0);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < UT; ++u) {
@@ -435,6 +478,17 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
         for (int r = 0; r < 3; ++r) {
           const int i = lk * 3 + r;
           if (i < W - 1) sc.tile[i * c + j] = S[r] * a.scale_log2;
+        }
+      }
+      if (due) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          const int i = lk * 3 + r;
+          const bool vis = valid && i < W - 1 && pv[u] <= a.t - W + 1 + i;
+          const float v = vis ? S[r] * a.scale_log2 : kNeg;
+          const float mn = fmaxf(wm[r], v);
+          wl[r] = wl[r] * exp2f(wm[r] - mn) + (vis ? exp2f(v - mn) : 0.f);
+          wm[r] = mn;
         }
       }
       const float sv = valid ? cur : kNeg;
@@ -474,6 +528,22 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
       cs.l[wave] = l_w;
     }
   }
+  if (due) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      float mm = wm[r];
+      mm = fmaxf(mm, dpp<0xB1>(mm));
+      mm = fmaxf(mm, dpp<0x4E>(mm));
+      mm = fmaxf(mm, dpp<0x141>(mm));
+      mm = fmaxf(mm, dpp<0x140>(mm));
+      const float ll = group_sum<16>(wl[r] * exp2f(wm[r] - mm));
+      const int i = lk * 3 + r;
+      if (li == 0 && i < W - 1) {
+        cs.wm[wave][i] = mm;
+        cs.wl[wave][i] = ll;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ k_step
@@ -481,8 +551,16 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
 // present (optional) and, if the stream is a Global stream at B + M slots, evict
 // (optional) — one launch.  Every thread reads the stream's metadata itself
 // (uniform scalar loads, no barrier); the query is requested first.
+template <class T, int D>
+struct StepWaves {
+  static constexpr int value =
+      sizeof(T) == 2 ? (D == 64 ? HKV_WPE_B64 : HKV_WPE_B128) : HKV_WPE_F32;
+};
+
 template <class T, int D, bool AP, bool AT, bool EV>
-__global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
+__global__ __launch_bounds__(kNT)
+__attribute__((amdgpu_waves_per_eu(StepWaves<T, D>::value, StepWaves<T, D>::value)))
+void k_step(StepArgs a) {
   using F = Frag<T>;
   constexpr int VE = F::N;           // elements per 16-byte fragment
   constexpr int G = D / VE;          // lanes per row
@@ -494,7 +572,6 @@ __global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
   __shared__ EvictShared es;
   __shared__ float lds_tile[EV ? kMaxWobs * kLdsSlots : 1];   // W x c floats, then keys
   __shared__ int lds_pos[EV ? kLdsSlots : 1];
-  __shared__ uint8_t lds_evf[EV ? kLdsSlots : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = a.s_begin + blockIdx.x;
@@ -574,8 +651,8 @@ __global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
 
   // eviction scratch of a due stream: on chip up to kLdsSlots slots
   const bool onchip = c <= kLdsSlots;
-  Scratch scr_l{lds_tile, lds_pos, reinterpret_cast<uint64_t*>(lds_tile), lds_evf};
-  Scratch scr_g{a.ws_tile + base * a.W, a.ws_pos + base, a.ws_keys + base, a.ws_evf + base};
+  Scratch scr_l{lds_tile, lds_pos, reinterpret_cast<uint64_t*>(lds_tile)};
+  Scratch scr_g{a.ws_tile + base * a.W, a.ws_pos + base, a.ws_keys + base};
   StepCtx x;
   x.base = base;
   x.s = s;
@@ -591,15 +668,18 @@ __global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
   // matrix cores — in the fused step this also yields its W x c scoring tile;
   // every other stream attends on the vector ALUs.  The choice depends on the
   // stream state only, so standalone and fused attention give identical bits.
-  const bool at_point = kMfma && AT && glob && c == B + a.M;
+  const bool at_point = kMfma && glob && c == B + a.M;
   const bool tile_here = at_point && EV && due && a.q_win != nullptr;
-  if (at_point) {
+  const bool mfma_pass = at_point && (AT || tile_here);
+  if (mfma_pass) {
+    // (a standalone eviction runs the same pass and discards its output, so the
+    // scores equal the fused step's bit for bit)
     if (onchip)
       attend_mfma<D, AP>(a, x, tile_here, scr_l, cs);
     else
       attend_mfma<D, AP>(a, x, tile_here, scr_g, cs);
   }
-  if (AT && !at_point) {
+  if (AT && !mfma_pass) {
     float qv[VE];
     {
       float qf[VE];
@@ -625,16 +705,22 @@ __global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
     for (int tt = t0; tt < t1; tt += U) {
       uint4 kr[U], vr[U];
       bool valid[U];
+      // branch-free: an invalid row (ragged tail, freed slot) reads row 0 of
+      // the stream and is zeroed, so all fragments of the tile are in flight
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int row = (tt + u) * R + g;
         valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
-        if (valid[u]) {
-          const bool fresh = AP && row == slot_new;
-          kr[u] = ld16(fresh ? knew : kbase + (long long)row * D * ES);
-          vr[u] = ld16(fresh ? vnew : vbase + (long long)row * D * ES);
+        const int rr = valid[u] ? row : 0;
+        const bool fresh = AP && rr == slot_new;
+        kr[u] = ld16(fresh ? knew : kbase + (long long)rr * D * ES);
+        vr[u] = ld16(fresh ? vnew : vbase + (long long)rr * D * ES);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!valid[u]) {
+          kr[u] = make_uint4(0, 0, 0, 0);
+          vr[u] = make_uint4(0, 0, 0, 0);
         }
       }
       float scr[U];
@@ -681,10 +767,22 @@ __global__ __launch_bounds__(kNT, HKV_WPE) void k_step(StepArgs a) {
       }
     }
   }
-  if (AT) {
+  if (AT || tile_here) {
     // combine the waves
     __syncthreads();
-    if (tid < D) {
+    if (tile_here && tid < a.W) {        // statistics of window query tid
+      const bool cur = tid == a.W - 1;
+      float Mq = kNeg;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2) Mq = fmaxf(Mq, cur ? cs.m[w2] : cs.wm[w2][tid]);
+      float Lq = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2)
+        Lq += (cur ? cs.l[w2] : cs.wl[w2][tid]) * exp2f((cur ? cs.m[w2] : cs.wm[w2][tid]) - Mq);
+      es.qm[tid] = Mq;
+      es.ql[tid] = Lq;
+    }
+    if (AT && tid < D) {
       float Mx = cs.m[0];
 #pragma unroll
       for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
@@ -997,7 +1095,6 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.ws_tile = reinterpret_cast<float*>(ws + d.ws_tile);
   a.ws_pos = reinterpret_cast<int*>(ws + d.ws_pos);
   a.ws_keys = reinterpret_cast<uint64_t*>(ws + d.ws_keys);
-  a.ws_evf = reinterpret_cast<uint8_t*>(ws + d.ws_evf);
   a.t = t;
   a.w = c->local_window;
   a.W = c->w_obs;
@@ -1184,6 +1281,10 @@ hkv_status hkv_ste_evict(const hkv_config* c, hkv_state* st, int32_t t, const vo
   dev::StepArgs a = step_args(c, st, d, t);
   a.q_win = static_cast<const char*>(q_win);
   a.ld_qw = ld_qw;
+  if (q_win) {                      // newest query of the window
+    a.q = a.q_win + (long long)(c->w_obs - 1) * c->head_dim * elem_bytes(c);
+    a.ld_q = ld_qw;
+  }
   a.log = log;
   a.s_begin = s_begin;
   launch_step<false, false, true>(c, a, s_count, static_cast<hipStream_t>(stream));

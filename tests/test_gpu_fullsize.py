@@ -1,0 +1,67 @@
+"""Full-size GPU parity: every workload at its real shape, in the launch
+configuration the benchmark times (one fused decode-step launch over all layers x
+sequences x heads per step).  The GPU runs the whole generation; the oracle
+replays a few sampled (layer, sequence) groups from the same seeded inputs and
+checks labels, counts, budgets, layouts, every eviction and every output of
+those groups."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from hkv_inputs.configs import WORKLOADS, full_cache_of
+from tests._parity import gpu_generation, group_streams, oracle_check_group
+
+SEED = 0
+
+
+def sampled_groups(w, n_extra=1):
+    """First and last group, plus a seeded random one."""
+    rng = np.random.default_rng(1234 + w.cid)
+    groups = [(0, 0), (w.layers - 1, w.batch - 1)]
+    for _ in range(n_extra):
+        groups.append((int(rng.integers(w.layers)), int(rng.integers(w.batch))))
+    return sorted(set(groups))
+
+
+CASES = ["tiny_f32", "llamagen_xl_rho1_6", "janus_pro_1b_rho1_4", "janus_pro_7b_rho1_6",
+         "janus_pro_7b_rho1_8", "lumina_mgpt_768_rho1_8"]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_fullsize_parity(name):
+    w = WORKLOADS[name]
+    groups = sampled_groups(w, n_extra=0 if name.startswith("lumina") else 1)
+    print(f"[gpu] full-size {name}: S={w.S} N={w.N} P={w.P} groups={groups}", flush=True)
+    g = gpu_generation(w, SEED, group_streams(w, groups))
+    torch.cuda.empty_cache()
+    rep = None
+    for (l, b) in groups:
+        rep = oracle_check_group(w, SEED, l, b, g, rep=rep)
+    labels = g.labels
+    print(f"  labels local/global {(labels == 0).sum()}/{(labels == 1).sum()} outputs "
+          f"{rep.outputs_checked} events {rep.events_checked} max err {rep.max_out_err:.3g} "
+          f"score err {rep.max_score_err:.3g} flags {rep.flagged_counts}/{rep.flagged_labels}/"
+          f"{rep.flagged_evictions}", flush=True)
+    assert not rep.failures, rep.failures[:8]
+    if name != "tiny_f32":
+        assert rep.events_checked > 0
+
+
+@pytest.mark.parametrize("name", ["llamagen_xl_rho1_6", "janus_pro_7b_rho1_6"])
+def test_fullsize_full_cache(name):
+    """The uncompressed baseline layout at full size (sampled group, first 96 steps)."""
+    w = full_cache_of(WORKLOADS[name])
+    groups = [(w.layers - 1, 0)]
+    print(f"[gpu] full-size full cache {w.name}", flush=True)
+    g = gpu_generation(w, SEED, group_streams(w, groups), steps=96)
+    torch.cuda.empty_cache()
+    rep = oracle_check_group(w, SEED, *groups[0], g, steps=96)
+    print(f"  outputs {rep.outputs_checked} max err {rep.max_out_err:.3g}", flush=True)
+    assert not rep.failures, rep.failures[:8]
