@@ -28,12 +28,19 @@ namespace hkv {
 namespace dev {
 
 // Tuning knobs (compile-time): waves per workgroup, row fragments in flight per
-// lane, key tiles in flight per wave on the matrix-core path.
+// lane (per element type and head size), key tiles in flight per wave on the
+// matrix-core path.
 #ifndef HKV_NW
 #define HKV_NW 4
 #endif
-#ifndef HKV_U
-#define HKV_U 2
+#ifndef HKV_U_B64
+#define HKV_U_B64 4
+#endif
+#ifndef HKV_U_B128
+#define HKV_U_B128 3
+#endif
+#ifndef HKV_U_F32
+#define HKV_U_F32 2
 #endif
 #ifndef HKV_UT
 #define HKV_UT 1
@@ -82,6 +89,10 @@ struct EvictShared {
   int cnt[2];
   int ne;
   float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / sum of each window query
+  uint64_t cand_key[2][kNW][kMaxEvict];  // per subset and wave: its bottom-q keys
+  int cand_slot[2][kNW][kMaxEvict];
+  int cand_n[2][kNW];
+  int ev_slot[kMaxEvict];              // evicted slots in ascending order
 };
 
 // Eviction key with the subset in the top bits: (subset << 62) | (score bits <<
@@ -95,20 +106,46 @@ __device__ inline int skey_sub(uint64_t k) { return int(k >> 62); }
 __device__ inline int skey_pos(uint64_t k) { return int(uint32_t(k) & 0x7fffffffu); }
 __device__ inline float skey_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 31) & 0x7fffffffu); }
 
+// Minimum of a 64-bit value over the wave, in every lane: DPP inside each
+// 16-lane row (quad xor 1, quad xor 2, half-row mirror, row mirror), then
+// swaps across rows.
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(x)), CTRL, 0xF, 0xF, true));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, true));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(x)), m));
+  const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(x >> 32)), m));
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ inline uint64_t wave_min_u64(uint64_t x) {
+  uint64_t y;
+  y = dpp_u64<0xB1>(x);  x = y < x ? y : x;
+  y = dpp_u64<0x4E>(x);  x = y < x ? y : x;
+  y = dpp_u64<0x141>(x); x = y < x ? y : x;
+  y = dpp_u64<0x140>(x); x = y < x ? y : x;
+  y = shfl_xor_u64(x, 16); x = y < x ? y : x;
+  y = shfl_xor_u64(x, 32); x = y < x ? y : x;
+  return x;
+}
+
 struct StepCtx {
   long long base;
   int s, lab, c, B, slot_new;          // c: slots holding a token (no free slot when due)
   bool glob, due;
 };
 
-// Per-slot scratch of an eviction: the W x c score tile (aliased by the keys
-// once the scores are formed) and the positions (reused as rank counters).  On chip (LDS)
-// for streams of at most kLdsSlots slots, else in the workspace; instantiating
-// both cases lets the compiler address the on-chip case with LDS instructions.
+// Per-slot scratch of an eviction: the W x c score tile and the positions.  On
+// chip (LDS) for streams of at most kLdsSlots slots, else in the workspace,
+// which then also holds the keys of the slots beyond the registers' share;
+// instantiating both cases lets the compiler address the on-chip case with LDS
+// instructions.
 struct Scratch {
   float* tile;
-  int* pos;                            // positions, then rank counters
-  uint64_t* keys;
+  int* pos;
+  uint64_t* keys;                      // used by streams beyond kLdsSlots only
 };
 
 // ------------------------------------------------------------------ eviction
@@ -117,7 +154,8 @@ struct Scratch {
 //      last W queries (query i at position t-W+1+i sees slots with pos <= its
 //      position), summed over the queries; without one, the state's scores;
 //   2. keys (subset, score, position); near/far sizes and quotas;
-//   3. rank of every candidate inside its subset; evicted iff rank < quota;
+//   3. the quota's lowest keys of each subset: each wave's own bottom-q, then
+//      the exact rank inside the union of the waves' candidates;
 //   4. the evicted slots are freed (position -1, listed ascending in the free
 //      list for the next appends); no row moves.  Returns n_free = M.
 template <class T, int D, bool AP>
@@ -238,11 +276,12 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   }
   __syncthreads();              // tile, positions and window statistics complete
 
-  // scores of the slots; the keys overwrite the tile, so read it first.  Each
-  // slot's position entry becomes its rank counter (read first by its owner).
+  // scores and keys of the slots.  Thread tid owns slots tid + k*kNT: the
+  // first SPT in registers, any further ones (streams beyond the on-chip size)
+  // as keys in the workspace, each read back only by the thread that wrote it.
   constexpr int SPT = (kLdsSlots + kNT - 1) / kNT;
-  float scv[SPT];
-  int pjv[SPT];
+  constexpr uint64_t kNone = ~0ull;    // no slot (subset field 3)
+  uint64_t kv[SPT];
   int nn = 0, nf = 0;
   auto score_of = [&](int j, int pj) {
     float v = 0.f;
@@ -261,36 +300,24 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const int j = tid + k * kNT;
-    scv[k] = 0.f;
-    pjv[k] = 0;
+    kv[k] = kNone;
     if (j < c) {
-      pjv[k] = sc.pos[j];
-      scv[k] = score_of(j, pjv[k]);
+      const int pj = sc.pos[j];
+      kv[k] = make_skey(sub_of(pj), score_of(j, pj), pj);
+    }
+    const int sb = int(kv[k] >> 62);
+    const uint64_t m0 = __ballot(sb == 0), m1 = __ballot(sb == 1);
+    if (lane == 0) {
+      nn += __popcll(m0);
+      nf += __popcll(m1);
     }
   }
-  for (int j = tid + SPT * kNT; j < c; j += kNT) {    // beyond the on-chip size: keys apart
+  for (int j = tid + SPT * kNT; j < c; j += kNT) {
     const int pj = sc.pos[j];
     const int sb = sub_of(pj);
     nn += sb == 0;
     nf += sb == 1;
     sc.keys[j] = make_skey(sb, score_of(j, pj), pj);
-    sc.pos[j] = 0;
-  }
-  __syncthreads();              // tile consumed
-#pragma unroll
-  for (int k = 0; k < SPT; ++k) {
-    const int j = tid + k * kNT;
-    const int sb = sub_of(pjv[k]);
-    const bool in = j < c;
-    if (in) {
-      sc.keys[j] = make_skey(sb, scv[k], pjv[k]);
-      sc.pos[j] = 0;
-    }
-    const uint64_t m0 = __ballot(in && sb == 0), m1 = __ballot(in && sb == 1);
-    if (lane == 0) {
-      nn += __popcll(m0);
-      nf += __popcll(m1);
-    }
   }
   if (c > SPT * kNT) {
     nn = wave_sum_int(nn);
@@ -300,7 +327,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     if (nn) atomicAdd(&es.cnt[0], nn);
     if (nf) atomicAdd(&es.cnt[1], nf);
   }
-  __syncthreads();              // keys, subset sizes, zeroed rank counters
+  __syncthreads();              // subset sizes
 
   // quotas: floor(M/2) near, the rest far; a short subset gives all it has
   const int E = a.M;
@@ -318,63 +345,109 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
     return 0;
   }
-  // rank of each candidate inside its subset (one key range per subset): P
-  // threads per slot, each counting over a share of the keys
-  const int P = c <= kNT ? kNT / c : 1;
-  const int len = (c + P - 1) / P;
-  for (int idx = tid; idx < c * P; idx += kNT) {
-    const int j = idx % c, part = idx / c;
-    const uint64_t kj = sc.keys[j];
-    const int sb = skey_sub(kj);
-    if (sb >= 2) continue;
-    const uint64_t lo = uint64_t(sb) << 62;
-    const int i0 = part * len, i1 = min(c, i0 + len);
-    int r = 0, i = i0;
-    for (; i + 8 <= i1; i += 8) {
-      uint64_t kk[8];
+
+  // bottom-q of each subset in two levels.  Every wave takes its own q smallest
+  // keys, one per round: the wave-wide minimum over the keys above the previous
+  // round's minimum (keys are unique).  The union over the waves holds the
+  // subset's q smallest; wave 0 ranks the union.
+  {
+    uint64_t prev0 = 0, prev1 = 0;
+    int n0 = 0, n1 = 0;
+    const int qmax = qn > qf ? qn : qf;
+    for (int r = 0; r < qmax; ++r) {
+      uint64_t my0 = kNone, my1 = kNone;
+      int j0 = 0, j1 = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kk[u] = sc.keys[i + u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r += (kk[u] >= lo) & (kk[u] < kj);
-    }
-    for (; i < i1; ++i) {
-      const uint64_t ki = sc.keys[i];
-      r += (ki >= lo) & (ki < kj);
-    }
-    if (r) atomicAdd(&sc.pos[j], r);
-  }
-  __syncthreads();
-  auto evicted = [&](int j) {
-    const uint64_t kj = sc.keys[j];
-    const int sb = skey_sub(kj);
-    return sb < 2 && sc.pos[j] < (sb == 0 ? qn : qf);
-  };
-  // the evicted slots, ascending: free list, log, positions
-  if (wave == 0) {
-    int ne = 0;
-    const uint64_t lt = lanemask_lt(lane);
-    for (int j0 = 0; j0 < c; j0 += kWave) {
-      const int j = j0 + lane;
-      const bool ev = j < c && evicted(j);
-      const uint64_t me = __ballot(ev);
-      if (ev) {
-        const int r = ne + __popcll(me & lt);
-        if (r < a.M) {
-          a.free_slots[(long long)s * a.M + r] = j;
-          if (a.log) a.log[(long long)s * a.M + r] = skey_pos(sc.keys[j]);
-        }
-        a.pos[base + j] = -1;
+      for (int k = 0; k < SPT; ++k) {
+        const uint64_t kk = kv[k];
+        const int sb = int(kk >> 62);
+        if (sb == 0 && (n0 == 0 || kk > prev0) && kk < my0) { my0 = kk; j0 = tid + k * kNT; }
+        if (sb == 1 && (n1 == 0 || kk > prev1) && kk < my1) { my1 = kk; j1 = tid + k * kNT; }
       }
-      ne += __popcll(me);
+      for (int j = tid + SPT * kNT; j < c; j += kNT) {
+        const uint64_t kk = sc.keys[j];
+        const int sb = int(kk >> 62);
+        if (sb == 0 && (n0 == 0 || kk > prev0) && kk < my0) { my0 = kk; j0 = j; }
+        if (sb == 1 && (n1 == 0 || kk > prev1) && kk < my1) { my1 = kk; j1 = j; }
+      }
+      const uint64_t m0 = wave_min_u64(r < qn ? my0 : kNone);
+      const uint64_t m1 = wave_min_u64(r < qf ? my1 : kNone);
+      if (m0 != kNone) {
+        if (my0 == m0) {
+          es.cand_key[0][wave][n0] = m0;
+          es.cand_slot[0][wave][n0] = j0;
+        }
+        prev0 = m0;
+        ++n0;
+      }
+      if (m1 != kNone) {
+        if (my1 == m1) {
+          es.cand_key[1][wave][n1] = m1;
+          es.cand_slot[1][wave][n1] = j1;
+        }
+        prev1 = m1;
+        ++n1;
+      }
     }
-    if (lane == 0) es.ne = ne;
+    if (lane == 0) {
+      es.cand_n[0][wave] = n0;
+      es.cand_n[1][wave] = n1;
+    }
+  }
+  __syncthreads();              // candidates of every wave
+
+  // wave 0: lanes 0-31 rank the near candidates, lanes 32-63 the far ones; the
+  // evicted slots are listed in ascending slot order (free list, log) and freed
+  static_assert(kNW * kMaxEvict <= 32, "candidate union must fit half a wave");
+  int ne_all = a.M;
+  if (wave == 0) {
+    const int sub = lane >> 5, e = lane & 31;
+    const int w0 = e / kMaxEvict, r0 = e % kMaxEvict;
+    const bool valid = w0 < kNW && r0 < es.cand_n[sub][w0];
+    const uint64_t mine = valid ? es.cand_key[sub][w0][r0] : kNone;
+    int rank = 0;
+    for (int w2 = 0; w2 < kNW; ++w2) {
+      const int n2 = es.cand_n[sub][w2];
+      for (int r2 = 0; r2 < n2; ++r2) rank += es.cand_key[sub][w2][r2] < mine;
+    }
+    const bool ev = valid && rank < (sub == 0 ? qn : qf);
+    const uint64_t evm = __ballot(ev);
+    const int ne = __popcll(evm);
+    const int j = ev ? es.cand_slot[sub][w0][r0] : 0;
+    int rs = 0;                                // rank of the slot among the evicted
+    for (uint64_t mm = evm; mm; mm &= mm - 1) {
+      const int l = __ffsll((unsigned long long)mm) - 1;
+      rs += __builtin_amdgcn_readlane(j, l) < j;
+    }
+    if (ev && rs < a.M) {
+      a.free_slots[(long long)s * a.M + rs] = j;
+      if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(mine);
+      a.pos[base + j] = -1;
+      es.ev_slot[rs] = j;
+    }
     if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
+    if (lane == 0) es.ne = ne;
+    ne_all = ne;
   }
   // with a log, the scores of the event (0 for the freed slots)
-  if (a.log)
-    for (int j = tid; j < c; j += kNT) a.score[base + j] = evicted(j) ? 0.0f : skey_score(sc.keys[j]);
-  __syncthreads();
-  if (es.ne != a.M) {
+  if (a.log) {
+    __syncthreads();            // freed slots listed
+    const int ne = es.ne;
+    auto freed = [&](int j) {
+      bool f = false;
+      for (int m = 0; m < ne && m < a.M; ++m) f |= es.ev_slot[m] == j;
+      return f;
+    };
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int j = tid + k * kNT;
+      if (j < c) a.score[base + j] = freed(j) ? 0.0f : skey_score(kv[k]);
+    }
+    for (int j = tid + SPT * kNT; j < c; j += kNT)
+      a.score[base + j] = freed(j) ? 0.0f : skey_score(sc.keys[j]);
+  }
+  // (only wave 0's value is used: the epilogue runs on thread 0)
+  if (ne_all != a.M) {
     if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
     return 0;
   }
@@ -556,6 +629,10 @@ struct StepWaves {
   static constexpr int value =
       sizeof(T) == 2 ? (D == 64 ? HKV_WPE_B64 : HKV_WPE_B128) : HKV_WPE_F32;
 };
+template <class T, int D>
+struct StepRows {
+  static constexpr int value = sizeof(T) == 2 ? (D == 64 ? HKV_U_B64 : HKV_U_B128) : HKV_U_F32;
+};
 
 template <class T, int D, bool AP, bool AT, bool EV>
 __global__ __launch_bounds__(kNT)
@@ -565,12 +642,12 @@ void k_step(StepArgs a) {
   constexpr int VE = F::N;           // elements per 16-byte fragment
   constexpr int G = D / VE;          // lanes per row
   constexpr int R = kWave / G;       // rows per wave instruction
-  constexpr int U = HKV_U;           // row fragments in flight per lane
+  constexpr int U = StepRows<T, D>::value;   // row fragments in flight per lane
   constexpr int ES = sizeof(T);
 
   __shared__ CombineShared cs;
   __shared__ EvictShared es;
-  __shared__ float lds_tile[EV ? kMaxWobs * kLdsSlots : 1];   // W x c floats, then keys
+  __shared__ float lds_tile[EV ? kMaxWobs * kLdsSlots : 1];   // W x c floats
   __shared__ int lds_pos[EV ? kLdsSlots : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -651,7 +728,7 @@ void k_step(StepArgs a) {
 
   // eviction scratch of a due stream: on chip up to kLdsSlots slots
   const bool onchip = c <= kLdsSlots;
-  Scratch scr_l{lds_tile, lds_pos, reinterpret_cast<uint64_t*>(lds_tile)};
+  Scratch scr_l{lds_tile, lds_pos, nullptr};
   Scratch scr_g{a.ws_tile + base * a.W, a.ws_pos + base, a.ws_keys + base};
   StepCtx x;
   x.base = base;
