@@ -396,34 +396,45 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   }
   __syncthreads();              // candidates of every wave
 
-  // wave 0: lanes 0-31 rank the near candidates, lanes 32-63 the far ones; the
-  // evicted slots are listed in ascending slot order (free list, log) and freed
-  static_assert(kNW * kMaxEvict <= 32, "candidate union must fit half a wave");
+  // wave 0 ranks each subset's candidates (lane e holds entry e of the union)
+  // and lists the evicted slots in ascending slot order (free list, log)
+  static_assert(kNW * kMaxEvict <= kWave, "candidate union must fit one wave");
   int ne_all = a.M;
   if (wave == 0) {
-    const int sub = lane >> 5, e = lane & 31;
-    const int w0 = e / kMaxEvict, r0 = e % kMaxEvict;
-    const bool valid = w0 < kNW && r0 < es.cand_n[sub][w0];
-    const uint64_t mine = valid ? es.cand_key[sub][w0][r0] : kNone;
-    int rank = 0;
-    for (int w2 = 0; w2 < kNW; ++w2) {
-      const int n2 = es.cand_n[sub][w2];
-      for (int r2 = 0; r2 < n2; ++r2) rank += es.cand_key[sub][w2][r2] < mine;
+    const int w0 = lane / kMaxEvict, r0 = lane % kMaxEvict;
+    bool ev[2];
+    int jv[2];
+    uint64_t key[2], evm[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const bool valid = w0 < kNW && r0 < es.cand_n[sb][w0];
+      key[sb] = valid ? es.cand_key[sb][w0][r0] : kNone;
+      int rank = 0;
+      for (int w2 = 0; w2 < kNW; ++w2) {
+        const int n2 = es.cand_n[sb][w2];
+        for (int r2 = 0; r2 < n2; ++r2) rank += es.cand_key[sb][w2][r2] < key[sb];
+      }
+      ev[sb] = valid && rank < (sb == 0 ? qn : qf);
+      evm[sb] = __ballot(ev[sb]);
+      jv[sb] = ev[sb] ? es.cand_slot[sb][w0][r0] : 0;
     }
-    const bool ev = valid && rank < (sub == 0 ? qn : qf);
-    const uint64_t evm = __ballot(ev);
-    const int ne = __popcll(evm);
-    const int j = ev ? es.cand_slot[sub][w0][r0] : 0;
-    int rs = 0;                                // rank of the slot among the evicted
-    for (uint64_t mm = evm; mm; mm &= mm - 1) {
-      const int l = __ffsll((unsigned long long)mm) - 1;
-      rs += __builtin_amdgcn_readlane(j, l) < j;
-    }
-    if (ev && rs < a.M) {
-      a.free_slots[(long long)s * a.M + rs] = j;
-      if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(mine);
-      a.pos[base + j] = -1;
-      es.ev_slot[rs] = j;
+    const int ne = __popcll(evm[0]) + __popcll(evm[1]);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int j = jv[sb];
+      int rs = 0;                              // rank of the slot among the evicted
+#pragma unroll
+      for (int sb2 = 0; sb2 < 2; ++sb2)
+        for (uint64_t mm = evm[sb2]; mm; mm &= mm - 1) {
+          const int l = __ffsll((unsigned long long)mm) - 1;
+          rs += __builtin_amdgcn_readlane(jv[sb2], l) < j;
+        }
+      if (ev[sb] && rs < a.M) {
+        a.free_slots[(long long)s * a.M + rs] = j;
+        if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(key[sb]);
+        a.pos[base + j] = -1;
+        es.ev_slot[rs] = j;
+      }
     }
     if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
     if (lane == 0) es.ne = ne;
