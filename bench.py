@@ -61,15 +61,17 @@ def step_bytes(labels, budgets, w):
     row = d * e
     base_bytes = lambda c: 2 * row * c + 2 * row + 2 * row + 8 + 33
     out = np.zeros(T)
-    glob = {}
+    glob, local = {}, {}
     for lab, B in zip(labels.tolist(), budgets.tolist()):
         if lab == 2:                       # full cache
             out += base_bytes(np.arange(P + 1, P + T + 1))
             continue
-        if lab == 0:                       # local ring
-            out += base_bytes(np.minimum(np.arange(P + 1, P + T + 1), w.local_window))
+        if lab == 0:                       # local ring of B slots
+            local[B] = local.get(B, 0) + 1
             continue
         glob[B] = glob.get(B, 0) + 1
+    for B, n in local.items():
+        out += n * base_bytes(np.minimum(np.arange(P + 1, P + T + 1), B))
     for B, n in glob.items():
         cnt = min(P, B)
         traj = np.zeros(T)
@@ -158,8 +160,9 @@ class Generation:
         self.qw = [self.Q.data_ptr() + (t - w.w_obs + 1 - (w.P - w.w_obs)) * d * eb
                    for t in range(w.N)]
 
-    def run(self, stream, events=None):
-        """One generation; `events` = (start, end) recorded around the decode loop."""
+    def run(self, stream, events=None, capture=None):
+        """One generation; `events` = (start, end) recorded around the decode loop;
+        `capture` ([steps, S, d], untimed use only) receives every step's output."""
         w, hk, st = self.w, self.hk, self.cache.state
         d = w.head_dim
         hk.hkv_classify(self.cfg, st, self.K, self.V, w.N * d, self.Q, w.q_rows * d, stream)
@@ -168,6 +171,8 @@ class Generation:
         for t in range(w.P, w.N):
             hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, self.qw[t],
                                w.q_rows * d, self.out, d, None, 0, w.S, stream)
+            if capture is not None:
+                capture[t - w.P].copy_(self.out)
         if events is not None:
             events[1].record(stream)
 
@@ -195,6 +200,30 @@ def time_generations(gen_obj, steps, warmup):
     return wall / steps * 1e3, loop_ms / gen_obj.w.steps
 
 
+def fidelity(comp, full):
+    """Relative L2 error of every compressed attention output against the
+    full-cache output of the same stream and step (one untimed generation each)."""
+    import torch
+    w = comp.w
+    stream = torch.cuda.current_stream()
+    a = torch.empty((w.steps, w.S, w.head_dim), dtype=comp.K.dtype, device=comp.K.device)
+    b = torch.empty_like(a)
+    comp.run(stream, capture=a)
+    full.run(stream, capture=b)
+    torch.cuda.synchronize()
+    a32, b32 = a.float(), b.float()
+    rel = (a32 - b32).norm(dim=-1) / b32.norm(dim=-1).clamp_min(1e-30)
+    q = torch.quantile(rel.flatten()[:: max(1, rel.numel() // 1_000_000)],
+                       torch.tensor([0.5, 0.99], device=rel.device))
+    return {"rel_l2_mean": round(float(rel.mean()), 6), "rel_l2_median": round(float(q[0]), 6),
+            "rel_l2_p99": round(float(q[1]), 6), "rel_l2_max": round(float(rel.max()), 6),
+            "what": "compressed vs full-cache attention output, every stream and step"}
+
+
+VARIANTS = {"headkv": (False, False), "unstratified": (True, False),
+            "uniform_budget": (False, True), "uniform_unstratified": (True, True)}
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the HBM counters."""
     import torch
@@ -219,6 +248,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-cache", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--variant", default="headkv", choices=sorted(VARIANTS),
+                    help="ablation: eviction without the near/far split and/or one budget "
+                         "for every head")
+    ap.add_argument("--fidelity", action="store_true",
+                    help="also report the attention-output error against the full cache")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -229,7 +263,7 @@ def main():
     import numpy as np
     import torch
     import kv_cache_compression_hkv_amd as hk
-    from hkv_inputs.configs import WORKLOADS, full_cache_of
+    from hkv_inputs.configs import WORKLOADS, full_cache_of, variant_of
     from hkv_inputs.gpu import device_inputs
 
     if args.copy_calibration:
@@ -237,6 +271,8 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.variant != "headkv":
+        w = variant_of(w, *VARIANTS[args.variant])
     torch.cuda.set_device(0)
     inputs = device_inputs(w, args.seed)
 
@@ -266,6 +302,7 @@ def main():
                    "head_dim": w.head_dim, "final_len": w.N, "prefill_len": w.P,
                    "rho": f"{w.rho[0]}/{w.rho[1]}", "decode_steps": w.steps,
                    "launch": "layer-folded, 1 fused launch per decode step",
+                   "variant": args.variant,
                    "global_batch": w.batch, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -278,6 +315,8 @@ def main():
     if not args.no_full_cache:
         wf = full_cache_of(w)
         full = Generation(wf, inputs, hk)
+        if args.fidelity:
+            res["fidelity"] = fidelity(comp, full)
         del comp
         torch.cuda.empty_cache()
         ms_f, launch_f = time_generations(full, max(2, args.steps // 2), 1)

@@ -43,6 +43,9 @@ class HkvConfig:
     p_local: Optional[float] = None
     anchor_mode: str = "prefill"   # "prefill" or "full_history"
     full_cache: bool = False       # baseline: no classification, no eviction
+    # ablation variants (same shapes; see the method notes of the library)
+    unstratified: bool = False     # eviction without the near/far split
+    uniform_budget: bool = False   # every head keeps floor(rho * N) tokens
 
     # ---- plain shape arithmetic (no method quantities) ----
     @property
@@ -117,3 +120,9 @@ WORKLOADS = {c.name: c for c in
 def full_cache_of(cfg: HkvConfig) -> HkvConfig:
     """The same workload laid out as an uncompressed cache (speed baseline)."""
     return cfg.with_(name=cfg.name + "_full", full_cache=True)
+
+
+def variant_of(cfg: HkvConfig, unstratified: bool = False, uniform_budget: bool = False) -> HkvConfig:
+    """The same workload run as an ablation variant."""
+    tag = ("_unstrat" if unstratified else "") + ("_uniform" if uniform_budget else "")
+    return cfg.with_(name=cfg.name + tag, unstratified=unstratified, uniform_budget=uniform_budget)

@@ -74,6 +74,20 @@ typedef enum {
 typedef enum { HKV_DT_BF16 = 0, HKV_DT_F32 = 1 } hkv_dtype;
 typedef enum { HKV_LOCAL = 0, HKV_GLOBAL = 1, HKV_FULL = 2 } hkv_label;
 
+/* Ablation variants (hkv_config.variant), for equal-memory comparisons with
+ * the two choices the pages credit (section "Key contributions", items 2 and 3):
+ *   HKV_VARIANT_UNSTRATIFIED    eviction without the near/far split: the M
+ *                               lowest (score, position) candidates over all
+ *                               candidates (same protected zone, same scores);
+ *   HKV_VARIANT_UNIFORM_BUDGET  every head gets the same budget A = floor(N*rho)
+ *                               (the fixed uniform per-head budget the pages
+ *                               ascribe to LineAR, section "Problem
+ *                               definition"): Local heads a ring of A slots,
+ *                               Global heads budget A.
+ * Classification, scores and layout rules are otherwise unchanged. */
+#define HKV_VARIANT_UNSTRATIFIED   1
+#define HKV_VARIANT_UNIFORM_BUDGET 2
+
 /* Device error bits in *err. */
 #define HKV_ERRBIT_CAPACITY 1   /* append into a full Global/FULL stream          */
 #define HKV_ERRBIT_LAYOUT   2   /* count/label/budget inconsistent                */
@@ -91,6 +105,7 @@ typedef struct {
   int32_t w_obs;                            /* W: scoring window (queries)      */
   int32_t evict_m;                          /* M: evictions per event (== W, even) */
   int32_t full_cache;                       /* 1: uncompressed baseline layout  */
+  int32_t variant;                          /* 0, or HKV_VARIANT_* bits (ablations) */
 } hkv_config;
 
 /* Cache state: device buffers owned by the caller (sizes from the helpers).

@@ -39,7 +39,8 @@ class hkv_config(ctypes.Structure):
                 ("head_dim", c_int32), ("dtype", c_int32), ("final_len", c_int32),
                 ("prefill_len", c_int32), ("local_window", c_int32), ("tau", c_float),
                 ("rho_num", c_int32), ("rho_den", c_int32), ("split_dist", c_int32),
-                ("w_obs", c_int32), ("evict_m", c_int32), ("full_cache", c_int32)]
+                ("w_obs", c_int32), ("evict_m", c_int32), ("full_cache", c_int32),
+                ("variant", c_int32)]
 
 
 class hkv_state(ctypes.Structure):
@@ -124,25 +125,32 @@ def hkv_last_error() -> str:
     return _lib.hkv_last_error().decode()
 
 
+VARIANT_UNSTRATIFIED = 1
+VARIANT_UNIFORM_BUDGET = 2
+
+
 def make_config(*, layers, batch, heads, head_dim, dtype, final_len, prefill_len,
                 local_window, tau, rho, split_dist, w_obs=8, evict_m=8,
-                full_cache=False) -> hkv_config:
-    """Build the C config.  dtype: "bf16" or "f32"; rho: (num, den)."""
+                full_cache=False, variant=0) -> hkv_config:
+    """Build the C config.  dtype: "bf16" or "f32"; rho: (num, den); variant:
+    0 or VARIANT_* bits."""
     return hkv_config(layers, batch, heads, head_dim,
                       DT_BF16 if dtype == "bf16" else DT_F32, final_len, prefill_len,
                       local_window, float(tau), int(rho[0]), int(rho[1]), split_dist, w_obs,
-                      evict_m, int(bool(full_cache)))
+                      evict_m, int(bool(full_cache)), int(variant))
 
 
 def config_from_workload(w) -> hkv_config:
     """C config from a workload description with the attributes layers, batch,
     heads, head_dim, dtype, N, P, local_window, tau, rho, split_dist, w_obs,
-    evict_m and full_cache."""
+    evict_m, full_cache, unstratified and uniform_budget."""
+    variant = ((VARIANT_UNSTRATIFIED if getattr(w, "unstratified", False) else 0) |
+               (VARIANT_UNIFORM_BUDGET if getattr(w, "uniform_budget", False) else 0))
     return make_config(layers=w.layers, batch=w.batch, heads=w.heads, head_dim=w.head_dim,
                        dtype=w.dtype, final_len=w.N, prefill_len=w.P,
                        local_window=w.local_window, tau=w.tau, rho=w.rho,
                        split_dist=w.split_dist, w_obs=w.w_obs, evict_m=w.evict_m,
-                       full_cache=w.full_cache)
+                       full_cache=w.full_cache, variant=variant)
 
 
 def hkv_pool_slots(cfg: hkv_config) -> int:

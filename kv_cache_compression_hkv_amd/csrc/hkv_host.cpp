@@ -1,6 +1,7 @@
 // Host-side core of the HeadKV C ABI (no HIP calls).
 #include "hkv_host.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -44,6 +45,8 @@ hkv_status derive(const hkv_config* c, Derived* d) {
     return fail(HKV_E_INVAL, "final_len must exceed prefill_len");
   if (c->full_cache != 0 && c->full_cache != 1)
     return fail(HKV_E_INVAL, "full_cache must be 0 or 1");
+  if (c->variant & ~(HKV_VARIANT_UNSTRATIFIED | HKV_VARIANT_UNIFORM_BUDGET))
+    return fail(HKV_E_INVAL, "variant has unknown bits 0x%x", c->variant);
   const int64_t S = int64_t(c->layers) * c->batch * c->heads;
   if (S > (int64_t(1) << 31) - 1) return fail(HKV_E_INVAL, "too many streams");
   d->S = S;
@@ -69,6 +72,9 @@ hkv_status derive(const hkv_config* c, Derived* d) {
                   (long long)A);
     d->A = int32_t(A);
     d->group_slots = int64_t(c->heads) * (A + c->evict_m);
+    // without the near/far split every candidate is near: with an empty far
+    // subset the quotas hand all evictions to the near one
+    d->split = (c->variant & HKV_VARIANT_UNSTRATIFIED) ? INT32_MAX : c->split_dist;
   }
   d->pool_slots = d->group_slots * c->layers * c->batch;
   size_t off = 0;

@@ -19,6 +19,7 @@ constexpr int kMaxHeads = 1024;
 struct Derived {
   int64_t S = 0;            // streams
   int32_t A = 0;            // floor(N * rho) per head (compressed only)
+  int32_t split = 0;        // near/far split distance in effect (variants)
   int64_t group_slots = 0;  // pool slots per (layer, sequence) group
   int64_t pool_slots = 0;
   // workspace layout (bytes from the workspace start, 256-B aligned)

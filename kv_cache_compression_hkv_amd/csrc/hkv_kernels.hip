@@ -686,9 +686,9 @@ void k_step(StepArgs a) {
   int ext = ext0, nf = nf0, slot_new = -1;
   bool ok = nf0 >= 0 && nf0 <= a.M;
   if (ok && AP) {
-    if (lab == HKV_LOCAL) {
-      slot_new = a.t % a.w;
-      ext = ext0 + 1 < a.w ? ext0 + 1 : a.w;
+    if (lab == HKV_LOCAL) {                   // ring of B slots (B = w, or A)
+      slot_new = a.t % B;
+      ext = ext0 + 1 < B ? ext0 + 1 : B;
     } else if (nf0 > 0) {                     // lowest freed slot
       slot_new = a.free_slots[(long long)s * a.M + (a.M - nf0)];
       nf = nf0 - 1;
@@ -1022,7 +1022,7 @@ struct LayoutArgs {
   long long* base; int* cap; int* count; int* budget; int* n_tokens; unsigned char* label;
   int* n_free;
   int* err;
-  int H, N, P, w, W, M, D, A, full;
+  int H, N, P, w, W, M, D, A, full, uniform;
   long long group_slots;
 };
 
@@ -1055,16 +1055,19 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
       int n_l = 0;
       for (int x = 0; x < a.H; ++x) n_l += lab[x] == HKV_LOCAL;
       const int n_g = a.H - n_l;
-      const int Bg = n_g ? (a.H * a.A - n_l * a.w) / n_g : 0;
+      // Local heads: ring of wl slots; Global heads: budget Bg (uniform
+      // variant: both floor(rho*N))
+      const int wl = a.uniform ? a.A : a.w;
+      const int Bg = a.uniform ? a.A : (n_g ? (a.H * a.A - n_l * a.w) / n_g : 0);
       long long off = (long long)grp * a.group_slots;
-      for (int x = 0; x < h; ++x) off += lab[x] == HKV_LOCAL ? a.w : Bg + a.M;
+      for (int x = 0; x < h; ++x) off += lab[x] == HKV_LOCAL ? wl : Bg + a.M;
       s_base = off;
       s_lab = lab[h];
       if (lab[h] == HKV_LOCAL) {
-        s_B = a.w;
-        s_count = P < a.w ? P : a.w;
+        s_B = wl;
+        s_count = P < wl ? P : wl;
         s_mode = 1;
-        a.cap[s] = a.w;
+        a.cap[s] = wl;
       } else {
         s_B = Bg;
         s_count = P <= Bg ? P : Bg;
@@ -1109,7 +1112,7 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
     __syncthreads();
   } else {
     for (int j = tid; j < P; j += kNT) {
-      if (mode == 1) dest[j] = (j >= P - a.w) ? j % a.w : -1;
+      if (mode == 1) dest[j] = (j >= P - s_B) ? j % s_B : -1;
       else dest[j] = j;
     }
     __syncthreads();
@@ -1187,7 +1190,7 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.w = c->local_window;
   a.W = c->w_obs;
   a.M = c->evict_m;
-  a.D = c->split_dist;
+  a.D = d.split;
   a.scale_log2 = scale_log2_of(c->head_dim);
   a.S = int(d.S);
   return a;
@@ -1290,9 +1293,10 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
   b.w = c->local_window;
   b.W = c->w_obs;
   b.M = c->evict_m;
-  b.D = c->split_dist;
+  b.D = d.split;
   b.A = d.A;
   b.full = c->full_cache;
+  b.uniform = (c->variant & HKV_VARIANT_UNIFORM_BUDGET) ? 1 : 0;
   b.group_slots = d.group_slots;
   const int n = int(d.S);
   if (c->dtype == HKV_DT_BF16) {

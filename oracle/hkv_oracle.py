@@ -24,6 +24,12 @@ carry the same text) by section:
               tokens evicted from each (for example M/2 and M/2).
   [Contrib/2] Key contributions, item 2: asymmetric budgets, compact for Local
               heads and larger for Global heads.
+  [Contrib/3] Key contributions, item 3: splitting by distance keeps informative
+              distant tokens that a single importance ranking tends to drop in
+              favour of local ones.
+  [Problem]   Problem definition: LineAR assigns one fixed, uniform budget to
+              every attention head (the allocation the uniform-budget ablation
+              reproduces).
   [Lay]       The lay explainer's statement that the cache keeps 1/4, 1/6 or 1/8
               of the original memory (the compression ratio rho).
 
@@ -36,7 +42,10 @@ spec choices the pages do not fix and are therefore "parity unpinned" as to
 their definition (only their internal consistency is pinned): the score formula
 (sum of the last W softmax probabilities), M = W, the Global budget split, the
 protected zone of the W newest tokens, the (score, position) tie-break and the
-slot layout (evicted slots are freed and refilled by the next tokens).
+slot layout (evicted slots are freed and refilled by the next tokens).  The two
+ablation variants (eviction without the near/far split; one budget for every
+head) are this project's readings of the comparisons the pages draw, pinned the
+same way.
 """
 from __future__ import annotations
 
@@ -131,6 +140,17 @@ def ste_select(slot_pos, slot_score, t: int, w_obs: int, split: int, n_evict: in
     return sorted(chosen)
 
 
+def unstratified_select(slot_pos, slot_score, t: int, w_obs: int, n_evict: int) -> List[int]:
+    """Ablation without the near/far split [Contrib/3]: the n_evict lowest
+    (score, position) candidates over all candidates, ascending slots.  Same
+    protected zone as ste_select (distance < w_obs is not a candidate)."""
+    cand = [j for j in range(len(slot_pos)) if t - slot_pos[j] >= w_obs]
+    if len(cand) < n_evict:
+        raise ValueError("fewer eviction candidates than evictions")
+    order = lambda j: (float(slot_score[j]), int(slot_pos[j]))
+    return sorted(sorted(cand, key=order)[:n_evict])
+
+
 def free_evicted(slot_pos, slot_score, evicted: List[int]):
     """Slot layout after an eviction (reading; the pages fix no layout): the
     evicted slots become free (position -1, score 0); no other slot moves.
@@ -217,6 +237,16 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
     D, tau = cfg.split_dist, cfg.tau
     num, den = cfg.rho
     per_head = (N * num) // den
+    # ablation variants: eviction without the near/far split [Contrib/3]; the
+    # same budget per_head for every head (the uniform allocation the pages
+    # attribute to LineAR, Problem definition) instead of [Contrib/2]
+    unstratified = getattr(cfg, "unstratified", False)
+    uniform = getattr(cfg, "uniform_budget", False)
+    ring = per_head if uniform else w          # Local window kept
+    if unstratified:
+        select = lambda table, sc, t, E: unstratified_select(table, sc, t, W, E)
+    else:
+        select = lambda table, sc, t, E: ste_select(table, sc, t, W, D, E)
     T = N - P if steps is None else steps
     rec = GroupRecord()
     q_at = lambda h, t: Q[h, t - (P - W)]
@@ -238,7 +268,12 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
                 labels[h] = lab
     rec.labels = list(labels)
     n_local = sum(1 for x in labels if x == LOCAL)
-    B = None if cfg.full_cache else global_budget(H, per_head, w, n_local)
+    if cfg.full_cache:
+        B = None
+    elif uniform:
+        B = per_head if n_local < H else None
+    else:
+        B = global_budget(H, per_head, w, n_local)
     rec.budget = B
 
     # ---- initial per-head layout ----
@@ -249,12 +284,12 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
             scores.append([0.0] * P)
             rec.caps.append(N)
         elif labels[h] == LOCAL:
-            ring = [-1] * w
-            for pos in range(max(0, P - w), P):
-                ring[pos % w] = pos
-            tables.append(ring)
-            scores.append([0.0] * w)
-            rec.caps.append(w)
+            slots = [-1] * ring
+            for pos in range(max(0, P - ring), P):
+                slots[pos % ring] = pos
+            tables.append(slots)
+            scores.append([0.0] * ring)
+            rec.caps.append(ring)
         else:
             rec.caps.append(B + M)
             sc = window_scores(Q[h, :W], K[h], P - W)
@@ -263,7 +298,7 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
                 scores.append(list(sc))
             else:
                 table = list(range(P))
-                own = ste_select(table, sc, P - 1, W, D, P - B)
+                own = select(table, sc, P - 1, P - B)
                 use = own
                 if evict_hook is not None:
                     alt = evict_hook(h, P - 1, table, list(sc), own)
@@ -285,7 +320,7 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
             q = q_at(h, t)
             lab = labels[h]
             if lab == LOCAL:
-                tables[h][t % w] = t
+                tables[h][t % ring] = t
             elif lab == FULL:
                 tables[h].append(t)
             else:
@@ -307,7 +342,7 @@ def run_group(cfg, K: np.ndarray, V: np.ndarray, Q: np.ndarray,
             for j, pj in zip(live, p):
                 scores[h][j] = float(scores[h][j]) + float(pj)
             if c == B + M:
-                own = ste_select(tables[h], scores[h], t, W, D, M)
+                own = select(tables[h], scores[h], t, M)
                 use = own
                 if evict_hook is not None:
                     alt = evict_hook(h, t, list(tables[h]), list(scores[h]), own)

@@ -163,6 +163,8 @@ def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
                        steps: Optional[int] = None, rep: Optional[Report] = None) -> Report:
     rep = rep or Report()
     H, P, W, D, N = w.heads, w.P, w.w_obs, w.split_dist, w.N
+    if getattr(w, "unstratified", False):       # one subset holds every candidate
+        D = 10 ** 9
     T = w.steps if steps is None else steps
     kb, vb, qb = gen.group_inputs(w, seed, l, b)
     K, Vv, Q = gen.decode(kb, w.dtype), gen.decode(vb, w.dtype), gen.decode(qb, w.dtype)

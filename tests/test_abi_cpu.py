@@ -64,6 +64,9 @@ def test_validate_workloads_and_sizes():
     (dict(split_dist=4), hk.E_INVAL),
     (dict(prefill_len=2000, final_len=3000), hk.E_UNSUPPORTED),
     (dict(local_window=0), hk.E_INVAL),
+    (dict(variant=hk.VARIANT_UNSTRATIFIED | hk.VARIANT_UNIFORM_BUDGET), hk.OK),
+    (dict(variant=4), hk.E_INVAL),         # unknown variant bit
+    (dict(variant=-1), hk.E_INVAL),
 ])
 def test_validate_rejects(kw, code):
     c = _cfg(**kw)

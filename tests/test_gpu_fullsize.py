@@ -15,7 +15,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
-from hkv_inputs.configs import WORKLOADS, full_cache_of
+from hkv_inputs.configs import WORKLOADS, full_cache_of, variant_of
 from tests._parity import gpu_generation, group_streams, oracle_check_group
 
 SEED = 0
@@ -65,3 +65,20 @@ def test_fullsize_full_cache(name):
     rep = oracle_check_group(w, SEED, *groups[0], g, steps=96)
     print(f"  outputs {rep.outputs_checked} max err {rep.max_out_err:.3g}", flush=True)
     assert not rep.failures, rep.failures[:8]
+
+
+@pytest.mark.parametrize("unstrat,uniform", [(True, False), (False, True)])
+def test_fullsize_variants(unstrat, uniform):
+    """The ablation variants at the LlamaGen-XL shape (sampled groups, all steps)."""
+    w = variant_of(WORKLOADS["llamagen_xl_rho1_6"], unstratified=unstrat, uniform_budget=uniform)
+    groups = sampled_groups(w, n_extra=0)
+    print(f"[gpu] full-size variant {w.name} groups={groups}", flush=True)
+    g = gpu_generation(w, SEED, group_streams(w, groups))
+    torch.cuda.empty_cache()
+    rep = None
+    for (l, b) in groups:
+        rep = oracle_check_group(w, SEED, l, b, g, rep=rep)
+    print(f"  events {rep.events_checked} max err {rep.max_out_err:.3g} "
+          f"flags {rep.flagged_counts}/{rep.flagged_labels}/{rep.flagged_evictions}", flush=True)
+    assert not rep.failures, rep.failures[:8]
+    assert rep.events_checked > 0

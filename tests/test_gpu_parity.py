@@ -44,6 +44,12 @@ CASES = {
     # Global streams longer than the on-chip scratch (spill to the workspace)
     "long_global": small_config(heads=2, prefix=0, image_tokens=1500, prefill_image=64,
                                 rho=(3, 4), split_dist=300, p_local=0.0),
+    # ablation variants: eviction without the near/far split; one budget for all
+    "unstratified": small_config(layers=2, batch=2, unstratified=True),
+    "uniform_budget": small_config(rho=(1, 6), split_dist=20, uniform_budget=True),
+    "uniform_unstrat_f32_d128": small_config(dtype="f32", head_dim=128, heads=4, rho=(1, 6),
+                                             p_local=0.0, unstratified=True,
+                                             uniform_budget=True),
 }
 
 

@@ -97,6 +97,17 @@ def _budget_ceil(heads, per_head, window, n_local):
 
 _ORIG_SELECT = O.ste_select
 
+
+def _unstrat_no_protection(slot_pos, slot_score, t, w_obs, n_evict):   # newest tokens eligible
+    order = lambda j: (float(slot_score[j]), int(slot_pos[j]))
+    return sorted(sorted(range(len(slot_pos)), key=order)[:n_evict])
+
+
+def _unstrat_highest(slot_pos, slot_score, t, w_obs, n_evict):         # keeps the lowest scores
+    cand = [j for j in range(len(slot_pos)) if t - slot_pos[j] >= w_obs]
+    order = lambda j: (-float(slot_score[j]), int(slot_pos[j]))
+    return sorted(sorted(cand, key=order)[:n_evict])
+
 MUTANTS = {
     "label_le": ("label_of", _label_le),
     "count_forward": ("classify_count", _count_forward),
@@ -113,6 +124,8 @@ MUTANTS = {
     "score_window_never_reset": ("scoring_window_starts", lambda *a: False),
     "score_window_late": ("scoring_window_starts",
                           lambda c, b, m, w: c == b + m - w + 2),
+    "unstrat_no_protection": ("unstratified_select", _unstrat_no_protection),
+    "unstrat_highest": ("unstratified_select", _unstrat_highest),
 }
 
 ALL_CHECKS = [
@@ -127,6 +140,8 @@ ALL_CHECKS = [
     lambda: pins.check_ste_golden(O),
     lambda: pins.check_ste_bruteforce(O, trials=60),
     lambda: pins.check_uniform_scores(O),
+    lambda: pins.check_unstratified_bruteforce(O, trials=60),
+    lambda: pins.check_variant_groups(O),
 ]
 
 

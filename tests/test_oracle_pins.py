@@ -319,6 +319,58 @@ def check_uniform_scores(orc):
         assert got == sorted(far[:4] + near[:4])
 
 
+# ---------------------------------------------------------------- ablation variants
+def check_unstratified_bruteforce(orc, trials=200):
+    """Without the near/far split the evicted set is the lexicographically
+    smallest E-subset of all candidates' (score, position) keys, enumerated
+    exhaustively; it equals the stratified choice with an unreachable split
+    (empty far subset, whose quota the shortfall rule hands to the near one)."""
+    rng = np.random.default_rng(23)
+    for _ in range(trials):
+        n = int(rng.integers(16, 21))
+        t, W = 100, 8
+        pos = sorted(rng.choice(np.arange(0, t + 1 - W), size=n - W, replace=False).tolist())
+        pos += list(range(t - W + 1, t + 1))
+        score = rng.integers(0, 5, size=n).astype(float) / 8.0   # many ties
+        E = int(rng.choice([2, 4, 6, 8]))
+        ev = orc.unstratified_select(pos, score, t, W, E)
+        cand = [j for j in range(n) if t - pos[j] >= W]
+        best = min(itertools.combinations(cand, E),
+                   key=lambda c: sorted((score[j], pos[j]) for j in c))
+        assert ev == sorted(best)
+        assert ev == orc.ste_select(pos, score, t, W, 10 ** 9, E)
+
+
+def check_variant_groups(orc):
+    """Group invariants of the ablation variants: the uniform variant keeps
+    exactly floor(rho*N) tokens in every head (Local rings of that size,
+    Global tables back at that budget after every eviction); the unstratified
+    variant evicts M candidates per event regardless of distance; scores still
+    sum to W and tables stay exact; and the variants do change decisions."""
+    base = dict(rho=(1, 6), split_dist=20)
+    cfg0, rec0, _, _ = run_small(orc, **base)
+    for unstrat, uniform in ((True, False), (False, True), (True, True)):
+        cfg, rec, K, Q = run_small(orc, unstratified=unstrat, uniform_budget=uniform, **base)
+        H, M, W = cfg.heads, cfg.evict_m, cfg.w_obs
+        A = (cfg.N * cfg.rho[0]) // cfg.rho[1]
+        if uniform:
+            assert rec.budget in (None, A)
+            for h in range(H):
+                want_cap = A if rec.labels[h] == orc.LOCAL else A + M
+                assert rec.caps[h] == want_cap
+                if rec.labels[h] == orc.LOCAL:
+                    t_last = cfg.N - 1
+                    assert sorted(rec.tables_final[h]) == list(range(t_last - A + 1, t_last + 1))
+        for ev in rec.events:
+            assert len(ev.slot_pos) == ev.budget + M
+            assert len(ev.evicted_slots) == M
+            assert min(ev.t - ev.slot_pos[j] for j in ev.evicted_slots) >= W
+        check_score_sum(orc, cfg, rec)
+        check_score_recompute(orc, cfg, rec, K, Q)
+        check_layout(orc, cfg, rec)
+        assert [e.evicted_slots for e in rec.events] != [e.evicted_slots for e in rec0.events]
+
+
 # ---------------------------------------------------------------- tests
 def test_uniform_count():
     check_uniform_count(O)
@@ -385,3 +437,11 @@ def test_pages_parameters():
         assert c.tau == tau
         assert c.rho in rhos
         assert c.evict_m % 2 == 0
+
+
+def test_unstratified_bruteforce():
+    check_unstratified_bruteforce(O)
+
+
+def test_variant_groups():
+    check_variant_groups(O)
