@@ -177,6 +177,67 @@ class Generation:
             events[1].record(stream)
 
 
+def decode_per_layer(gen_obj, stream):
+    """The decode loop as a model runs it: at every step one launch per layer,
+    each over that layer's batch x heads streams."""
+    w, hk, st = gen_obj.w, gen_obj.hk, gen_obj.cache.state
+    d, per = w.head_dim, w.batch * w.heads
+    for t in range(w.P, w.N):
+        for l in range(w.layers):
+            hk.hkv_decode_step(gen_obj.cfg, st, t, gen_obj.kp[t], gen_obj.vp[t], w.N * d,
+                               gen_obj.qw[t], w.q_rows * d, gen_obj.out, d, None, l * per, per,
+                               stream)
+
+
+def time_per_layer(gen_obj, steps):
+    """Per-layer decode loop, launched eagerly and replayed as one HIP graph
+    (captured once; every replay follows an eager classification)."""
+    import numpy as np
+    import torch
+    w, hk = gen_obj.w, gen_obj.hk
+    d = w.head_dim
+    cur = torch.cuda.current_stream()
+
+    def classify():
+        hk.hkv_classify(gen_obj.cfg, gen_obj.cache.state, gen_obj.K, gen_obj.V, w.N * d,
+                        gen_obj.Q, w.q_rows * d, cur)
+
+    def timed(body):
+        out = []
+        for k in range(steps + 1):                       # first one warms up
+            classify()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            body()
+            b.record(cur)
+            b.synchronize()
+            if k:
+                out.append(a.elapsed_time(b))
+        hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
+        return float(np.mean(out))
+
+    eager = timed(lambda: decode_per_layer(gen_obj, cur))
+    classify()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(side):
+        graph.capture_begin()
+        decode_per_layer(gen_obj, side)
+        graph.capture_end()
+    torch.cuda.synchronize()
+    capture_s = time.perf_counter() - t0
+    replay = timed(graph.replay)
+    launches = w.steps * w.layers
+    return {"launches_per_step": w.layers, "streams_per_launch": w.batch * w.heads,
+            "eager_ms_per_gen": round(eager, 3), "graph_ms_per_gen": round(replay, 3),
+            "graph_tokens_per_s": round(w.batch * w.steps / (replay * 1e-3), 1),
+            "graph_us_per_launch": round(replay * 1e3 / launches, 3),
+            "capture_s": round(capture_s, 2)}
+
+
 def time_generations(gen_obj, steps, warmup):
     """Mean ms per generation over `steps` timed generations, and the mean
     duration of one decode-step launch (HIP events bracketing each generation's
@@ -253,6 +314,8 @@ def main():
                          "for every head")
     ap.add_argument("--fidelity", action="store_true",
                     help="also report the attention-output error against the full cache")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="also time the per-layer decode loop, eager and as a HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -312,6 +375,8 @@ def main():
                      "alg_bytes_per_launch": round(float(alg.mean()), 1)},
         "labels": {"local": int((labels == 0).sum()), "global": int((labels == 1).sum())},
     }
+    if args.per_layer:
+        res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2))
     if not args.no_full_cache:
         wf = full_cache_of(w)
         full = Generation(wf, inputs, hk)
