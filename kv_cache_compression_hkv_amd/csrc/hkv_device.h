@@ -46,6 +46,35 @@ struct Frag<float> {
 };
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming load of a 16-byte fragment that is read once per launch (cached K/V
+// rows): non-temporal, so it does not displace the small per-stream data that
+// every launch reads again.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+#ifndef HKV_NT_LOADS
+#define HKV_NT_LOADS 1
+#endif
+__device__ inline uint4 ld16_stream(const void* p) {
+#if HKV_NT_LOADS
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return ld16(p);
+#endif
+}
+// The same for the other data read once per launch (queries, the appended
+// row's source); a separate switch so that each can be measured alone.
+#ifndef HKV_NT_ONCE
+#define HKV_NT_ONCE 1
+#endif
+__device__ inline uint4 ld16_once(const void* p) {
+#if HKV_NT_ONCE
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return ld16(p);
+#endif
+}
 __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // ---------------------------------------------------------------- reductions

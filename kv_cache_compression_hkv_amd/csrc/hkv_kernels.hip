@@ -498,7 +498,7 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
   bf16x8 qa[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
-    qa[kc] = __builtin_bit_cast(bf16x8, qsrc ? ld16(qsrc + (lk * 8 + kc * 32) * ES)
+    qa[kc] = __builtin_bit_cast(bf16x8, qsrc ? ld16_once(qsrc + (lk * 8 + kc * 32) * ES)
                                              : make_uint4(0, 0, 0, 0));
 
   const char* knew = a.k_new + (long long)s * a.ld_kv * ES;
@@ -530,8 +530,8 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
       const char* vr = fresh ? vnew : a.v_pool + (base + jj) * D * ES;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        kb[u][kc] = ld16(kr + (lk * 8 + kc * 32) * ES);
-        vb[u][kc] = ld16(vr + (lk * 8 + kc * 32) * ES);
+        kb[u][kc] = ld16_stream(kr + (lk * 8 + kc * 32) * ES);
+        vb[u][kc] = ld16_stream(vr + (lk * 8 + kc * 32) * ES);
       }
       pv[u] = 0;
       if (due) pv[u] = fresh ? a.t : a.pos[base + jj];
@@ -668,7 +668,7 @@ void k_step(StepArgs a) {
   constexpr bool kMfma = sizeof(T) == 2;     // bf16: eviction steps attend on the matrix cores
   // query fragment first: its address does not depend on the stream metadata
   uint4 q_raw = make_uint4(0, 0, 0, 0);
-  if (AT) q_raw = ld16(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
+  if (AT) q_raw = ld16_once(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
 
   // the label byte through the scalar path (aligned 32-bit word), except in a
   // last partial word
@@ -729,7 +729,7 @@ void k_step(StepArgs a) {
       const int sb = tid % G;
       const char* src = (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sb * VE) * ES;
       char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * D + sb * VE) * ES;
-      st16(dst, ld16(src));
+      st16(dst, ld16_once(src));
     }
     if (tid == 0) {
       a.pos[base + slot_new] = a.t;
@@ -801,8 +801,8 @@ void k_step(StepArgs a) {
         valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
         const int rr = valid[u] ? row : 0;
         const bool fresh = AP && rr == slot_new;
-        kr[u] = ld16(fresh ? knew : kbase + (long long)rr * D * ES);
-        vr[u] = ld16(fresh ? vnew : vbase + (long long)rr * D * ES);
+        kr[u] = ld16_stream(fresh ? knew : kbase + (long long)rr * D * ES);
+        vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * D * ES);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
