@@ -60,6 +60,25 @@ namespace dev {
 constexpr int kNW = HKV_NW;            // waves per workgroup
 constexpr int kNT = kNW * kWave;
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
+// block b runs on XCD b % 8.  Mapping each XCD to a contiguous run of streams
+// keeps the streams that share a cache line of per-stream data (16 per 64 B)
+// on one L2.  A bijection of [0, n).
+#ifndef HKV_XCD_REMAP
+#define HKV_XCD_REMAP 1
+#endif
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int n) {
+#if HKV_XCD_REMAP
+  const int x = b % kXcds, i = b / kXcds;
+  const int q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + i;
+#else
+  (void)n;
+  return b;
+#endif
+}
+
 struct StepArgs {
   const char* k_new; const char* v_new; long long ld_kv;   // ld in elements
   const char* q; long long ld_q;                            // current query
@@ -662,7 +681,7 @@ void k_step(StepArgs a) {
   __shared__ int lds_pos[EV ? kLdsSlots : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = a.s_begin + blockIdx.x;
+  const int s = a.s_begin + xcd_block(blockIdx.x, gridDim.x);
   const int g = lane / G, sub = lane % G;
 
   constexpr bool kMfma = sizeof(T) == 2;     // bf16: eviction steps attend on the matrix cores
