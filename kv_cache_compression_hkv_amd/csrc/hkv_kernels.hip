@@ -110,7 +110,6 @@ struct EvictShared {
   float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / sum of each window query
   uint64_t cand_key[2][kNW][kMaxEvict];  // per subset and wave: its bottom-q keys
   int cand_slot[2][kNW][kMaxEvict];
-  int cand_n[2][kNW];
   int ev_slot[kMaxEvict];              // evicted slots in ascending order
 };
 
@@ -125,18 +124,18 @@ __device__ inline int skey_sub(uint64_t k) { return int(k >> 62); }
 __device__ inline int skey_pos(uint64_t k) { return int(uint32_t(k) & 0x7fffffffu); }
 __device__ inline float skey_score(uint64_t k) { return __uint_as_float(uint32_t(k >> 31) & 0x7fffffffu); }
 
-// Minimum of a 64-bit value over the wave, in every lane: DPP inside each
-// 16-lane row (quad xor 1, quad xor 2, half-row mirror, row mirror), then
-// swaps across rows.
+// Minimum of a 64-bit value over the wave (uniform result): DPP inside each
+// 16-lane row (quad xor 1, quad xor 2, half-row mirror, row mirror), then the
+// four row minima read out to scalars.
 template <int CTRL>
 __device__ inline uint64_t dpp_u64(uint64_t x) {
   const uint32_t lo = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(x)), CTRL, 0xF, 0xF, true));
   const uint32_t hi = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(x >> 32)), CTRL, 0xF, 0xF, true));
   return (uint64_t(hi) << 32) | lo;
 }
-__device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = uint32_t(__shfl_xor(int(uint32_t(x)), m));
-  const uint32_t hi = uint32_t(__shfl_xor(int(uint32_t(x >> 32)), m));
+__device__ inline uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(x >> 32)), l));
   return (uint64_t(hi) << 32) | lo;
 }
 __device__ inline uint64_t wave_min_u64(uint64_t x) {
@@ -145,9 +144,13 @@ __device__ inline uint64_t wave_min_u64(uint64_t x) {
   y = dpp_u64<0x4E>(x);  x = y < x ? y : x;
   y = dpp_u64<0x141>(x); x = y < x ? y : x;
   y = dpp_u64<0x140>(x); x = y < x ? y : x;
-  y = shfl_xor_u64(x, 16); x = y < x ? y : x;
-  y = shfl_xor_u64(x, 32); x = y < x ? y : x;
-  return x;
+  uint64_t m = readlane_u64(x, 0);
+#pragma unroll
+  for (int r = 16; r < kWave; r += 16) {
+    const uint64_t v = readlane_u64(x, r);
+    m = v < m ? v : m;
+  }
+  return m;
 }
 
 struct StepCtx {
@@ -346,6 +349,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     if (nn) atomicAdd(&es.cnt[0], nn);
     if (nf) atomicAdd(&es.cnt[1], nf);
   }
+  if (tid < 2 * kNW * kMaxEvict) (&es.cand_key[0][0][0])[tid] = kNone;   // unused entries
   __syncthreads();              // subset sizes
 
   // quotas: floor(M/2) near, the rest far; a short subset gives all it has
@@ -408,52 +412,36 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         ++n1;
       }
     }
-    if (lane == 0) {
-      es.cand_n[0][wave] = n0;
-      es.cand_n[1][wave] = n1;
-    }
   }
   __syncthreads();              // candidates of every wave
 
-  // wave 0 ranks each subset's candidates (lane e holds entry e of the union)
-  // and lists the evicted slots in ascending slot order (free list, log)
-  static_assert(kNW * kMaxEvict <= kWave, "candidate union must fit one wave");
+  // wave 0: lanes 0-31 rank the near candidates, lanes 32-63 the far ones
+  // (entry e of the union; unused entries hold kNone); the evicted slots are
+  // listed in ascending slot order (free list, log) and freed
+  static_assert(kNW * kMaxEvict <= 32, "candidate union must fit half a wave");
   int ne_all = a.M;
   if (wave == 0) {
-    const int w0 = lane / kMaxEvict, r0 = lane % kMaxEvict;
-    bool ev[2];
-    int jv[2];
-    uint64_t key[2], evm[2];
+    constexpr int NC = kNW * kMaxEvict;
+    const int sub = lane >> 5, e = lane & 31;
+    const uint64_t* ck = &es.cand_key[sub][0][0];
+    const uint64_t mine = e < NC ? ck[e] : kNone;
+    int rank = 0;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const bool valid = w0 < kNW && r0 < es.cand_n[sb][w0];
-      key[sb] = valid ? es.cand_key[sb][w0][r0] : kNone;
-      int rank = 0;
-      for (int w2 = 0; w2 < kNW; ++w2) {
-        const int n2 = es.cand_n[sb][w2];
-        for (int r2 = 0; r2 < n2; ++r2) rank += es.cand_key[sb][w2][r2] < key[sb];
-      }
-      ev[sb] = valid && rank < (sb == 0 ? qn : qf);
-      evm[sb] = __ballot(ev[sb]);
-      jv[sb] = ev[sb] ? es.cand_slot[sb][w0][r0] : 0;
+    for (int e2 = 0; e2 < NC; ++e2) rank += ck[e2] < mine;
+    const bool ev = mine != kNone && rank < (sub == 0 ? qn : qf);
+    const uint64_t evm = __ballot(ev);
+    const int ne = __popcll(evm);
+    const int j = ev ? (&es.cand_slot[sub][0][0])[e] : 0;
+    int rs = 0;                                // rank of the slot among the evicted
+    for (uint64_t mm = evm; mm; mm &= mm - 1) {
+      const int l = __ffsll((unsigned long long)mm) - 1;
+      rs += __builtin_amdgcn_readlane(j, l) < j;
     }
-    const int ne = __popcll(evm[0]) + __popcll(evm[1]);
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int j = jv[sb];
-      int rs = 0;                              // rank of the slot among the evicted
-#pragma unroll
-      for (int sb2 = 0; sb2 < 2; ++sb2)
-        for (uint64_t mm = evm[sb2]; mm; mm &= mm - 1) {
-          const int l = __ffsll((unsigned long long)mm) - 1;
-          rs += __builtin_amdgcn_readlane(jv[sb2], l) < j;
-        }
-      if (ev[sb] && rs < a.M) {
-        a.free_slots[(long long)s * a.M + rs] = j;
-        if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(key[sb]);
-        a.pos[base + j] = -1;
-        es.ev_slot[rs] = j;
-      }
+    if (ev && rs < a.M) {
+      a.free_slots[(long long)s * a.M + rs] = j;
+      if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(mine);
+      a.pos[base + j] = -1;
+      es.ev_slot[rs] = j;
     }
     if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
     if (lane == 0) es.ne = ne;
