@@ -52,7 +52,7 @@ namespace dev {
 #define HKV_WPE_B64 6
 #endif
 #ifndef HKV_WPE_B128
-#define HKV_WPE_B128 4
+#define HKV_WPE_B128 5
 #endif
 #ifndef HKV_WPE_F32
 #define HKV_WPE_F32 4
@@ -651,6 +651,23 @@ template <class T, int D>
 struct StepRows {
   static constexpr int value = sizeof(T) == 2 ? (D == 64 ? HKV_U_B64 : HKV_U_B128) : HKV_U_F32;
 };
+// Attention of a bf16 Global stream at its eviction point on the matrix cores
+// (one pass yields the output and the W x c scoring tile), or on the vector
+// ALUs like every other stream, the eviction then forming the tile in a second
+// matrix-core pass over K (loaded with caching in the first).  The first keeps
+// the d64 kernel at 6 waves/SIMD; for d128 its registers would cap the whole
+// kernel at 4 waves, the second runs at 5.  Measured on MI355X.
+#ifndef HKV_MFMA_ATTN_B64
+#define HKV_MFMA_ATTN_B64 1
+#endif
+#ifndef HKV_MFMA_ATTN_B128
+#define HKV_MFMA_ATTN_B128 0
+#endif
+template <class T, int D>
+struct StepMfmaAttn {
+  static constexpr bool value =
+      sizeof(T) == 2 && (D == 64 ? HKV_MFMA_ATTN_B64 != 0 : HKV_MFMA_ATTN_B128 != 0);
+};
 
 template <class T, int D, bool AP, bool AT, bool EV>
 __global__ __launch_bounds__(kNT)
@@ -672,7 +689,7 @@ void k_step(StepArgs a) {
   const int s = a.s_begin + xcd_block(blockIdx.x, gridDim.x);
   const int g = lane / G, sub = lane % G;
 
-  constexpr bool kMfma = sizeof(T) == 2;     // bf16: eviction steps attend on the matrix cores
+  constexpr bool kMfma = StepMfmaAttn<T, D>::value;  // eviction-point attention on the matrix cores
   // query fragment first: its address does not depend on the stream metadata
   uint4 q_raw = make_uint4(0, 0, 0, 0);
   if (AT) q_raw = ld16_once(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
@@ -759,10 +776,12 @@ void k_step(StepArgs a) {
   x.due = due;
 
   // ---------------- attention over slots [0, c)
-  // A bf16 Global stream at its eviction point (c == B + M) attends on the
-  // matrix cores — in the fused step this also yields its W x c scoring tile;
-  // every other stream attends on the vector ALUs.  The choice depends on the
-  // stream state only, so standalone and fused attention give identical bits.
+  // With kMfma a bf16 Global stream at its eviction point (c == B + M) attends
+  // on the matrix cores — in the fused step this also yields its W x c scoring
+  // tile; every other stream attends on the vector ALUs.  The choice depends on
+  // the stream state only, so standalone and fused attention give identical
+  // bits.  Without kMfma a due stream keeps its K rows in the caches for the
+  // eviction's own tile pass.
   const bool at_point = kMfma && glob && c == B + a.M;
   const bool tile_here = at_point && EV && due && a.q_win != nullptr;
   const bool mfma_pass = at_point && (AT || tile_here);
@@ -791,6 +810,7 @@ void k_step(StepArgs a) {
     const int per = (ntiles + kNW - 1) / kNW;
     const int t0 = wave * per;
     const int t1 = min(ntiles, t0 + per);
+    const bool keep_k = !kMfma && EV && due && a.q_win != nullptr;
 
     float m_run = kNeg, l_run = 0.f;
     float acc[VE];
@@ -808,7 +828,8 @@ void k_step(StepArgs a) {
         valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
         const int rr = valid[u] ? row : 0;
         const bool fresh = AP && rr == slot_new;
-        kr[u] = ld16_stream(fresh ? knew : kbase + (long long)rr * D * ES);
+        kr[u] = keep_k ? ld16(fresh ? knew : kbase + (long long)rr * D * ES)
+                       : ld16_stream(fresh ? knew : kbase + (long long)rr * D * ES);
         vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * D * ES);
       }
 #pragma unroll
