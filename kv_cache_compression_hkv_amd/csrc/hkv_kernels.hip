@@ -107,7 +107,7 @@ struct CombineShared {
 struct EvictShared {
   int cnt[2];
   int ne;
-  float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / sum of each window query
+  float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / 1/sum of each window query
   uint64_t cand_key[2][kNW][kMaxEvict];  // per subset and wave: its bottom-q keys
   int cand_slot[2][kNW][kMaxEvict];
   int ev_slot[kMaxEvict];              // evicted slots in ascending order
@@ -292,7 +292,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       l = wave_sum(l);
       if (lane == 0) {
         es.qm[i] = m;
-        es.ql[i] = l;
+        es.ql[i] = 1.0f / l;
       }
     }
   }
@@ -308,8 +308,9 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   auto score_of = [&](int j, int pj) {
     float v = 0.f;
     if (window) {
-      for (int i = 0; i < W; ++i)
-        if (pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * (1.0f / es.ql[i]);
+#pragma unroll
+      for (int i = 0; i < kMaxWobs; ++i)
+        if (i < W && pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * es.ql[i];
     } else {
       v = (AP && j == slot_new) ? 0.0f : a.score[base + j];
     }
@@ -896,7 +897,7 @@ void k_step(StepArgs a) {
       for (int w2 = 0; w2 < kNW; ++w2)
         Lq += (cur ? cs.l[w2] : cs.wl[w2][tid]) * exp2f((cur ? cs.m[w2] : cs.wm[w2][tid]) - Mq);
       es.qm[tid] = Mq;
-      es.ql[tid] = Lq;
+      es.ql[tid] = 1.0f / Lq;
     }
     if (AT && tid < D) {
       float Mx = cs.m[0];
