@@ -108,6 +108,7 @@ struct EvictShared {
   int cnt[2];
   int ne;
   float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / 1/sum of each window query
+  float pm[kNW][kMaxWobs], pl[kNW][kMaxWobs];   // per-wave partials of the tile pass
   uint64_t cand_key[2][kNW][kMaxEvict];  // per subset and wave: its bottom-q keys
   int cand_slot[2][kNW][kMaxEvict];
   int ev_slot[kMaxEvict];              // evicted slots in ascending order
@@ -221,24 +222,65 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       }
       const char* knew = a.k_new + ((long long)s * a.ld_kv) * ES;
       const int ntile = (c + 15) / 16;
-      for (int kt = wave; kt < ntile; kt += kNW) {
-        const int j = kt * 16 + li;
-        const char* row = (AP && j == slot_new) ? knew : a.k_pool + ((base + j) * D) * ES;
-        uint4 kb[KC];
+      // UE key tiles in flight per wave (clamped addresses, zeroed when out of
+      // range); each lane keeps online softmax statistics of its 4 query rows
+      // over the slots each query sees
+      constexpr int UE = 2;
+      float wm[4], wl[4];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          kb[kc] = j < c ? ld16(row + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) {
+        wm[r] = kNeg;
+        wl[r] = 0.f;
+      }
+      for (int kt0 = wave; kt0 < ntile; kt0 += kNW * UE) {
+        uint4 kb[UE][KC];
+        int pj[UE];
+        bool vj[UE];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[kc]),
-                                                        acc, 0, 0, 0);
-        if (j < c) {
+        for (int u = 0; u < UE; ++u) {
+          const int j = (kt0 + u * kNW) * 16 + li;
+          vj[u] = kt0 + u * kNW < ntile && j < c;
+          const int jj = vj[u] ? j : 0;
+          const bool fresh = AP && jj == slot_new;
+          const char* row = fresh ? knew : a.k_pool + ((base + jj) * D) * ES;
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) kb[u][kc] = ld16(row + (lk * 8 + kc * 32) * ES);
+          pj[u] = fresh ? t : a.pos[base + jj];
+        }
+#pragma unroll
+        for (int u = 0; u < UE; ++u) {
+          const int j = (kt0 + u * kNW) * 16 + li;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[u][kc]),
+                                                          acc, 0, 0, 0);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = lk * 4 + r;
-            if (i < W) sc.tile[i * c + j] = acc[r] * a.scale_log2;
+            const float v = acc[r] * a.scale_log2;
+            if (vj[u] && i < W) sc.tile[i * c + j] = v;
+            const bool vis = vj[u] && i < W && pj[u] <= t - W + 1 + i;
+            const float vv = vis ? v : kNeg;
+            const float mn = fmaxf(wm[r], vv);
+            wl[r] = wl[r] * exp2f(wm[r] - mn) + (vis ? exp2f(vv - mn) : 0.f);
+            wm[r] = mn;
           }
+        }
+      }
+      // statistics over the 16 key columns of each row group, then per wave
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mm = wm[r];
+        mm = fmaxf(mm, dpp<0xB1>(mm));
+        mm = fmaxf(mm, dpp<0x4E>(mm));
+        mm = fmaxf(mm, dpp<0x141>(mm));
+        mm = fmaxf(mm, dpp<0x140>(mm));
+        const float ll = group_sum<16>(wl[r] * exp2f(wm[r] - mm));
+        const int i = lk * 4 + r;
+        if (li == 0 && i < W) {
+          es.pm[wave][i] = mm;
+          es.pl[wave][i] = ll;
         }
       }
     } else {
@@ -277,7 +319,19 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       }
     }
   }
-  if (window && !tile_ready) {
+  if (window && !tile_ready && sizeof(T) == 2) {
+    __syncthreads();
+    if (tid < W) {                     // combine the waves' statistics of query tid
+      float M = kNeg;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2) M = fmaxf(M, es.pm[w2][tid]);
+      float L = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kNW; ++w2) L += es.pl[w2][tid] * exp2f(es.pm[w2][tid] - M);
+      es.qm[tid] = M;
+      es.ql[tid] = 1.0f / L;
+    }
+  } else if (window && !tile_ready) {
     __syncthreads();
     // softmax statistics of each window query over the slots it sees
     for (int i = wave; i < W; i += kNW) {
