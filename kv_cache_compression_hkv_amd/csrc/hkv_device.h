@@ -11,7 +11,6 @@ namespace dev {
 
 constexpr int kWave = 64;
 constexpr float kNeg = -3.0e38f;       // finite "minus infinity" for masked logits
-constexpr int kLdsSlots = 512;         // Global streams up to this size keep eviction scratch on chip
 
 // ---------------------------------------------------------------- element types
 // A lane moves one 16-byte fragment of a row: 8 bf16 or 4 fp32 values.

@@ -36,8 +36,11 @@ namespace dev {
 #ifndef HKV_U_B64
 #define HKV_U_B64 4
 #endif
-#ifndef HKV_U_B128
-#define HKV_U_B128 3
+#ifndef HKV_U_B128S            // bf16 d128, short streams
+#define HKV_U_B128S 2
+#endif
+#ifndef HKV_U_B128L            // bf16 d128, long streams
+#define HKV_U_B128L 3
 #endif
 #ifndef HKV_U_F32
 #define HKV_U_F32 2
@@ -51,8 +54,11 @@ namespace dev {
 #ifndef HKV_WPE_B64
 #define HKV_WPE_B64 6
 #endif
-#ifndef HKV_WPE_B128
-#define HKV_WPE_B128 5
+#ifndef HKV_WPE_B128S
+#define HKV_WPE_B128S 8
+#endif
+#ifndef HKV_WPE_B128L
+#define HKV_WPE_B128L 5
 #endif
 #ifndef HKV_WPE_F32
 #define HKV_WPE_F32 4
@@ -60,6 +66,14 @@ namespace dev {
 constexpr int kNW = HKV_NW;            // waves per workgroup
 constexpr int kNT = kNW * kWave;
 
+// Key tiles in flight per wave in the eviction's matrix-core passes (bf16 d128,
+// short / long streams).
+#ifndef HKV_UE_S
+#define HKV_UE_S 1
+#endif
+#ifndef HKV_UE_L
+#define HKV_UE_L 2
+#endif
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
 // block b runs on XCD b % 8.  Mapping each XCD to a contiguous run of streams
 // keeps the streams that share a cache line of per-stream data (16 per 64 B)
@@ -160,15 +174,15 @@ struct StepCtx {
   bool glob, due;
 };
 
-// Per-slot scratch of an eviction: the W x c score tile and the positions.  On
-// chip (LDS) for streams of at most kLdsSlots slots, else in the workspace,
-// which then also holds the keys of the slots beyond the registers' share;
-// instantiating both cases lets the compiler address the on-chip case with LDS
-// instructions.
+// Per-slot scratch of an eviction: the W x c logit tile and the positions, or
+// (when the eviction forms the keys itself) the keys.  On chip (LDS) for
+// streams up to the kernel's on-chip size, else in the workspace, which then
+// also holds the keys of the slots beyond the registers' share; instantiating
+// both cases lets the compiler address the on-chip case with LDS instructions.
 struct Scratch {
   float* tile;
   int* pos;
-  uint64_t* keys;                      // used by streams beyond kLdsSlots only
+  uint64_t* keys;
 };
 
 // ------------------------------------------------------------------ eviction
@@ -181,9 +195,78 @@ struct Scratch {
 //      the exact rank inside the union of the waves' candidates;
 //   4. the evicted slots are freed (position -1, listed ascending in the free
 //      list for the next appends); no row moves.  Returns n_free = M.
-template <class T, int D, bool AP>
+// Attention of a bf16 Global stream at its eviction point on the matrix cores
+// (one pass yields the output and the W x c scoring tile), or on the vector
+// ALUs like every other stream, the eviction then forming the tile in a second
+// matrix-core pass over K (loaded with caching in the first).  The first keeps
+// the d64 kernel at 6 waves/SIMD; for d128 its registers would cap the whole
+// kernel at 4 waves, the second runs at 8 (short streams) or 5 (long).
+// Measured on MI355X.
+#ifndef HKV_MFMA_ATTN_B64
+#define HKV_MFMA_ATTN_B64 1
+#endif
+#ifndef HKV_MFMA_ATTN_B128
+#define HKV_MFMA_ATTN_B128 0
+#endif
+template <class T, int D>
+struct StepMfmaAttn {
+  static constexpr bool value =
+      sizeof(T) == 2 && (D == 64 ? HKV_MFMA_ATTN_B64 != 0 : HKV_MFMA_ATTN_B128 != 0);
+};
+
+// Shape of the decode step per element type, head size and stream class C.
+// bf16 d128 has two: short streams (C = 0) run 8 waves/SIMD with 2 rows in
+// flight per lane, long streams (C = 1) 5 waves with 3; the host picks the class
+// from the configured budget.
+//
+// How an eviction scores its slots, and how many its scratch holds on chip.
+// bf16 with the attention on the vector ALUs (kKeys): on the matrix cores, either
+// in one pass that keeps the W x c logit tile on chip (short streams up to
+// kOnePass slots) or in two passes over K, the first for each window query's
+// softmax statistics and the second writing each slot's key directly (8 bytes
+// per slot, in the same on-chip buffer).  Otherwise the tile and the positions
+// (36 bytes per slot) come from the attention (bf16 d64) or a vector-ALU pass
+// (fp32).  Sizes measured on MI355X: the d128 short-stream kernel's LDS stays
+// small enough for 8 workgroups per CU.
+#ifndef HKV_ONCHIP_KEYS
+#define HKV_ONCHIP_KEYS 1024
+#endif
+#ifndef HKV_ONEPASS_S
+#define HKV_ONEPASS_S 256
+#endif
+#ifndef HKV_ONCHIP_TILE_B16
+#define HKV_ONCHIP_TILE_B16 512
+#endif
+#ifndef HKV_ONCHIP_TILE_F32
+#define HKV_ONCHIP_TILE_F32 512
+#endif
+template <class T, int D, int C>
+struct StepCfg {
+  static constexpr bool kB16 = sizeof(T) == 2;
+  static constexpr int kWaves =
+      !kB16 ? HKV_WPE_F32 : (D == 64 ? HKV_WPE_B64 : (C ? HKV_WPE_B128L : HKV_WPE_B128S));
+  static constexpr int kRows =
+      !kB16 ? HKV_U_F32 : (D == 64 ? HKV_U_B64 : (C ? HKV_U_B128L : HKV_U_B128S));
+  static constexpr int kTilesInFlight = C ? HKV_UE_L : HKV_UE_S;
+  static constexpr bool kKeys = kB16 && !StepMfmaAttn<T, D>::value;
+  static constexpr int kOnePass = kKeys && !C ? HKV_ONEPASS_S : 0;
+  static constexpr int kSlots =
+      kKeys ? HKV_ONCHIP_KEYS : (kB16 ? HKV_ONCHIP_TILE_B16 : HKV_ONCHIP_TILE_F32);
+  static_assert(!kKeys || kMaxWobs * kOnePass * 4 <= kSlots * 8, "tile fits the keys buffer");
+};
+
+// Window queries of a bf16 stream staged on chip for the eviction's score tile:
+// W rows of D elements, 16 bytes of padding per row so that the 16-byte reads of
+// consecutive rows fall in distinct banks.
+template <int D>
+struct QStage {
+  static constexpr int kPitch = D / 4 + 2;   // row pitch in 8-byte units
+};
+
+template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
-                                            EvictShared& es, bool tile_ready) {
+                                            EvictShared& es, bool tile_ready, uint2* qs,
+                                            bool q_staged) {
   // (returns the number of freed slots: M, or 0 if nothing was evicted)
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
@@ -194,81 +277,115 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   const int t = a.t, W = a.W, Dd = a.D;
 
   if (tid < 2) es.cnt[tid] = 0;
-
-  // positions of all slots (already staged by the attention when tile_ready)
-  if (!tile_ready)
-    for (int j = tid; j < c; j += kNT) sc.pos[j] = (AP && j == slot_new) ? t : a.pos[base + j];
-
   const bool window = a.q_win != nullptr;
-  if (window && tile_ready) {
-    // the W x c tile was produced by the attention's matrix-core pass
-  } else if (window) {
-    if constexpr (sizeof(T) == 2) {
-      // bf16: the W x c logit tile on the matrix cores.  v_mfma_f32_16x16x32_bf16:
-      // A = the W queries (rows W..15 zero), B = 16 keys per tile, K = 32 head
-      // elements per instruction; lane l holds A row l%16 and B column l%16 at
-      // elements (l/16)*8 .. +7, and receives D rows (l/16)*4 .. +3, column l%16.
+  constexpr uint64_t kNone = ~0ull;    // no slot (subset field 3)
+  // slots tid + k*kNT, k < SPT, have their keys in registers for the selection;
+  // any further ones are read from the scratch keys
+  constexpr int SPT = 2;
+  uint64_t kv[SPT];
+  auto sub_of = [&](int pj) {
+    const int dist = t - pj;
+    return dist < W ? 2 : (dist < Dd ? 0 : 1);
+  };
+
+  using OC = StepCfg<T, D, C>;
+  if constexpr (OC::kKeys) {
+    // bf16 with the attention on the vector ALUs.  With a query window the
+    // matrix cores form the logits: in one pass that also keeps the W x c tile
+    // and the positions on chip (streams up to kOnePass slots), or in two, the
+    // second writing the keys directly to the scratch.  Without one the keys
+    // come from the state's scores.
+    int nn = 0, nf = 0;                // subset sizes seen by this wave
+    const bool one_pass = window && c <= OC::kOnePass;
+    if (window) {
+      // v_mfma_f32_16x16x32_bf16: A = the W queries (rows W..15 zero), B = 16
+      // keys per tile, K = 32 head elements per instruction; lane l holds A row
+      // l%16 and B column l%16 at elements (l/16)*8 .. +7, and receives D rows
+      // (l/16)*4 .. +3, column l%16.
       typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
       typedef float f32x4 __attribute__((ext_vector_type(4)));
       constexpr int KC = D / 32;
       const int li = lane % 16, lk = lane / 16;
-      bf16x8 qa[KC];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (li < W)
-          u = ld16(a.q_win + ((long long)s * a.ld_qw + (long long)li * D + lk * 8 + kc * 32) * ES);
-        qa[kc] = __builtin_bit_cast(bf16x8, u);
+      constexpr int QP = QStage<D>::kPitch;
+      if (!q_staged) {
+        // (a standalone eviction stages the window queries here)
+        const int qrow = tid / (D / 4), qcol = tid % (D / 4);
+        if (qrow < W)
+          qs[qrow * QP + qcol] = *reinterpret_cast<const uint2*>(
+              a.q_win + ((long long)s * a.ld_qw + (long long)qrow * D + qcol * 4) * ES);
+        __syncthreads();
       }
+      // A operand chunk kc of this lane: query row li, elements lk*8 + kc*32 .. +7,
+      // read from the staged rows at each use (rows W..15 are zero)
+      auto qa_of = [&](int kc) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (li < W) u = *reinterpret_cast<const uint4*>(qs + li * QP + lk * 2 + kc * 8);
+        return __builtin_bit_cast(bf16x8, u);
+      };
       const char* knew = a.k_new + ((long long)s * a.ld_kv) * ES;
       const int ntile = (c + 15) / 16;
-      // UE key tiles in flight per wave (clamped addresses, zeroed when out of
-      // range); each lane keeps online softmax statistics of its 4 query rows
-      // over the slots each query sees
-      constexpr int UE = 2;
+      // one pass over the slots' key tiles: UE tiles in flight per wave (absent
+      // tiles skipped, ragged columns zeroed); body(j, valid, position, logits)
+      auto tiles = [&](auto&& body) {
+        constexpr int UE = OC::kTilesInFlight;
+        for (int kt0 = wave; kt0 < ntile; kt0 += kNW * UE) {
+          uint4 kb[UE][KC];
+          int pj[UE];
+          bool vj[UE];
+#pragma unroll
+          for (int u = 0; u < UE; ++u) {
+            const int j = (kt0 + u * kNW) * 16 + li;
+            const bool tile_in = kt0 + u * kNW < ntile;     // uniform across the wave
+            vj[u] = tile_in && j < c;
+            if (tile_in) {
+              const int jj = vj[u] ? j : 0;
+              const bool fresh = AP && jj == slot_new;
+              const char* row = fresh ? knew : a.k_pool + ((base + jj) * D) * ES;
+#pragma unroll
+              for (int kc = 0; kc < KC; ++kc) kb[u][kc] = ld16(row + (lk * 8 + kc * 32) * ES);
+              pj[u] = fresh ? t : a.pos[base + jj];
+            } else {
+#pragma unroll
+              for (int kc = 0; kc < KC; ++kc) kb[u][kc] = make_uint4(0, 0, 0, 0);
+              pj[u] = 0;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < UE; ++u) {
+            if (kt0 + u * kNW >= ntile) break;                // uniform
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_of(kc), __builtin_bit_cast(bf16x8, kb[u][kc]),
+                                                            acc, 0, 0, 0);
+            body((kt0 + u * kNW) * 16 + li, vj[u], pj[u], acc);
+          }
+        }
+      };
+
+      // pass 1: each lane's online softmax statistics of its 4 query rows over
+      // the slots each query sees; reduced over the 16 key columns, then waves
+      // (one pass: also the tile and the positions)
       float wm[4], wl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         wm[r] = kNeg;
         wl[r] = 0.f;
       }
-      for (int kt0 = wave; kt0 < ntile; kt0 += kNW * UE) {
-        uint4 kb[UE][KC];
-        int pj[UE];
-        bool vj[UE];
+      tiles([&](int j, bool vj, int pj, const f32x4& acc) {
+        if (one_pass && lk == 0 && vj) sc.pos[j] = pj;
 #pragma unroll
-        for (int u = 0; u < UE; ++u) {
-          const int j = (kt0 + u * kNW) * 16 + li;
-          vj[u] = kt0 + u * kNW < ntile && j < c;
-          const int jj = vj[u] ? j : 0;
-          const bool fresh = AP && jj == slot_new;
-          const char* row = fresh ? knew : a.k_pool + ((base + jj) * D) * ES;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) kb[u][kc] = ld16(row + (lk * 8 + kc * 32) * ES);
-          pj[u] = fresh ? t : a.pos[base + jj];
+        for (int r = 0; r < 4; ++r) {
+          const int i = lk * 4 + r;
+          const float v = acc[r] * a.scale_log2;
+          if (one_pass && vj && i < W) sc.tile[i * c + j] = v;
+          const bool vis = vj && i < W && pj <= t - W + 1 + i;
+          const float vv = vis ? v : kNeg;
+          const float mn = fmaxf(wm[r], vv);
+          wl[r] = wl[r] * exp2f(wm[r] - mn) + (vis ? exp2f(vv - mn) : 0.f);
+          wm[r] = mn;
         }
-#pragma unroll
-        for (int u = 0; u < UE; ++u) {
-          const int j = (kt0 + u * kNW) * 16 + li;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[u][kc]),
-                                                          acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = lk * 4 + r;
-            const float v = acc[r] * a.scale_log2;
-            if (vj[u] && i < W) sc.tile[i * c + j] = v;
-            const bool vis = vj[u] && i < W && pj[u] <= t - W + 1 + i;
-            const float vv = vis ? v : kNeg;
-            const float mn = fmaxf(wm[r], vv);
-            wl[r] = wl[r] * exp2f(wm[r] - mn) + (vis ? exp2f(vv - mn) : 0.f);
-            wm[r] = mn;
-          }
-        }
-      }
-      // statistics over the 16 key columns of each row group, then per wave
+      });
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float mm = wm[r];
@@ -283,129 +400,203 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
           es.pl[wave][i] = ll;
         }
       }
-    } else {
-      // fp32: each lane keeps its fragment of every window query in registers
-      float qf[kMaxWobs][VE];
+      __syncthreads();
+      if (tid < W) {                   // combine the waves' statistics of query tid
+        float M = kNeg;
 #pragma unroll
-      for (int i = 0; i < kMaxWobs; ++i) {
-        float tmp[VE];
-        if (i < W) {
-          F::to_f32(ld16(a.q_win + ((long long)s * a.ld_qw + (long long)i * D + sub * VE) * ES), tmp);
-        } else {
+        for (int w2 = 0; w2 < kNW; ++w2) M = fmaxf(M, es.pm[w2][tid]);
+        float L = 0.f;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) tmp[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < VE; ++e) qf[i][e] = tmp[e] * a.scale_log2;
+        for (int w2 = 0; w2 < kNW; ++w2) L += es.pl[w2][tid] * exp2f(es.pm[w2][tid] - M);
+        es.qm[tid] = M;
+        es.ql[tid] = 1.0f / L;
       }
-      const char* kbase = a.k_pool + (base * D + sub * VE) * ES;
-      const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
-      for (int j0 = wave * R; j0 < c; j0 += kNW * R) {
-        const int j = j0 + g;
-        if (j < c) {
-          float kf[VE];
-          F::to_f32(ld16((AP && j == slot_new) ? knew : kbase + (long long)j * D * ES), kf);
-          float mine = 0.f;
-#pragma unroll
-          for (int i = 0; i < kMaxWobs; ++i) {
-            float d0 = 0.f;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) d0 = fmaf(qf[i][e], kf[e], d0);
-            d0 = group_sum<G>(d0);
-            if (i == sub) mine = d0;
-          }
-          if (sub < W) sc.tile[sub * c + j] = mine;
-        }
-      }
-    }
-  }
-  if (window && !tile_ready && sizeof(T) == 2) {
-    __syncthreads();
-    if (tid < W) {                     // combine the waves' statistics of query tid
-      float M = kNeg;
-#pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2) M = fmaxf(M, es.pm[w2][tid]);
-      float L = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2) L += es.pl[w2][tid] * exp2f(es.pm[w2][tid] - M);
-      es.qm[tid] = M;
-      es.ql[tid] = 1.0f / L;
-    }
-  } else if (window && !tile_ready) {
-    __syncthreads();
-    // softmax statistics of each window query over the slots it sees
-    for (int i = wave; i < W; i += kNW) {
-      const int lim = t - W + 1 + i;
-      float m = kNeg;
-      for (int j = lane; j < c; j += kWave)
-        if (sc.pos[j] <= lim) m = fmaxf(m, sc.tile[i * c + j]);
-      m = wave_max(m);
-      float l = 0.f;
-      for (int j = lane; j < c; j += kWave)
-        if (sc.pos[j] <= lim) l += exp2f(sc.tile[i * c + j] - m);
-      l = wave_sum(l);
-      if (lane == 0) {
-        es.qm[i] = m;
-        es.ql[i] = 1.0f / l;
-      }
-    }
-  }
-  __syncthreads();              // tile, positions and window statistics complete
+      __syncthreads();                 // window statistics (and tile) complete
 
-  // scores and keys of the slots.  Thread tid owns slots tid + k*kNT: the
-  // first SPT in registers, any further ones (streams beyond the on-chip size)
-  // as keys in the workspace, each read back only by the thread that wrote it.
-  constexpr int SPT = (kLdsSlots + kNT - 1) / kNT;
-  constexpr uint64_t kNone = ~0ull;    // no slot (subset field 3)
-  uint64_t kv[SPT];
-  int nn = 0, nf = 0;
-  auto score_of = [&](int j, int pj) {
-    float v = 0.f;
-    if (window) {
+      if (one_pass) {
+        // scores from the tile: thread tid owns slots tid + k*kNT
 #pragma unroll
-      for (int i = 0; i < kMaxWobs; ++i)
-        if (i < W && pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * es.ql[i];
+        for (int k = 0; k < SPT; ++k) {
+          const int j = tid + k * kNT;
+          kv[k] = kNone;
+          if (j < c) {
+            const int pj = sc.pos[j];
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < kMaxWobs; ++i)
+              if (i < W && pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * es.ql[i];
+            kv[k] = make_skey(sub_of(pj), v, pj);
+          }
+          const int sb = int(kv[k] >> 62);
+          nn += __popcll(__ballot(sb == 0));
+          nf += __popcll(__ballot(sb == 1));
+        }
+      } else {
+        // pass 2: the same logits, now as probabilities summed over each slot's
+        // visible queries (rows 0-3 in lanes 0-15, rows 4-7 in lanes 16-31);
+        // lanes 0-15 write the keys
+        float qm_r[4], ql_r[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = lk * 4 + r;
+          qm_r[r] = i < W ? es.qm[i] : 0.f;
+          ql_r[r] = i < W ? es.ql[i] : 0.f;
+        }
+        tiles([&](int j, bool vj, int pj, const f32x4& acc) {
+          float pr = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = lk * 4 + r;
+            if (vj && i < W && pj <= t - W + 1 + i) pr += exp2f(acc[r] * a.scale_log2 - qm_r[r]) * ql_r[r];
+          }
+          pr += __shfl_xor(pr, 16);
+          const bool own = lk == 0 && vj;
+          const int sb = sub_of(pj);
+          if (own) sc.keys[j] = make_skey(sb, pr, pj);
+          nn += __popcll(__ballot(own && sb == 0));
+          nf += __popcll(__ballot(own && sb == 1));
+        });
+      }
     } else {
-      v = (AP && j == slot_new) ? 0.0f : a.score[base + j];
+      for (int j0 = wave * kWave; j0 < c; j0 += kNT) {
+        const int j = j0 + lane;
+        const bool own = j < c;
+        const bool fresh = AP && j == slot_new;
+        const int pj = own ? (fresh ? t : a.pos[base + j]) : 0;
+        const int sb = sub_of(pj);
+        if (own) sc.keys[j] = make_skey(sb, fresh ? 0.0f : a.score[base + j], pj);
+        nn += __popcll(__ballot(own && sb == 0));
+        nf += __popcll(__ballot(own && sb == 1));
+      }
     }
-    return v;
-  };
-  auto sub_of = [&](int pj) {
-    const int dist = t - pj;
-    return dist < W ? 2 : (dist < Dd ? 0 : 1);
-  };
-#pragma unroll
-  for (int k = 0; k < SPT; ++k) {
-    const int j = tid + k * kNT;
-    kv[k] = kNone;
-    if (j < c) {
-      const int pj = sc.pos[j];
-      kv[k] = make_skey(sub_of(pj), score_of(j, pj), pj);
-    }
-    const int sb = int(kv[k] >> 62);
-    const uint64_t m0 = __ballot(sb == 0), m1 = __ballot(sb == 1);
     if (lane == 0) {
-      nn += __popcll(m0);
-      nf += __popcll(m1);
+      if (nn) atomicAdd(&es.cnt[0], nn);
+      if (nf) atomicAdd(&es.cnt[1], nf);
     }
+    if (tid < 2 * kNW * kMaxEvict) (&es.cand_key[0][0][0])[tid] = kNone;   // unused entries
+    __syncthreads();                   // keys and subset sizes
+    if (!one_pass) {
+#pragma unroll
+      for (int k = 0; k < SPT; ++k) {
+        const int j = tid + k * kNT;
+        kv[k] = j < c ? sc.keys[j] : kNone;
+      }
+    }
+  } else {
+    // the W x c tile of logits, then the scores.  Positions of all slots
+    // (already staged by the attention when tile_ready).
+    if (!tile_ready)
+      for (int j = tid; j < c; j += kNT) sc.pos[j] = (AP && j == slot_new) ? t : a.pos[base + j];
+    if (window && !tile_ready) {
+      if constexpr (StepMfmaAttn<T, D>::value) {
+        // the attention's matrix-core pass always delivers this tile
+        if (tid == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
+        if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
+        return 0;
+      } else {
+        // fp32: each lane keeps its fragment of every window query in registers
+        float qf[kMaxWobs][VE];
+#pragma unroll
+        for (int i = 0; i < kMaxWobs; ++i) {
+          float tmp[VE];
+          if (i < W) {
+            F::to_f32(ld16(a.q_win + ((long long)s * a.ld_qw + (long long)i * D + sub * VE) * ES), tmp);
+          } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) tmp[e] = 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < VE; ++e) qf[i][e] = tmp[e] * a.scale_log2;
+        }
+        const char* kbase = a.k_pool + (base * D + sub * VE) * ES;
+        const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
+        for (int j0 = wave * R; j0 < c; j0 += kNW * R) {
+          const int j = j0 + g;
+          if (j < c) {
+            float kf[VE];
+            F::to_f32(ld16((AP && j == slot_new) ? knew : kbase + (long long)j * D * ES), kf);
+            float mine = 0.f;
+#pragma unroll
+            for (int i = 0; i < kMaxWobs; ++i) {
+              float d0 = 0.f;
+#pragma unroll
+              for (int e = 0; e < VE; ++e) d0 = fmaf(qf[i][e], kf[e], d0);
+              d0 = group_sum<G>(d0);
+              if (i == sub) mine = d0;
+            }
+            if (sub < W) sc.tile[sub * c + j] = mine;
+          }
+        }
+      }
+      __syncthreads();
+      // softmax statistics of each window query over the slots it sees
+      for (int i = wave; i < W; i += kNW) {
+        const int lim = t - W + 1 + i;
+        float m = kNeg;
+        for (int j = lane; j < c; j += kWave)
+          if (sc.pos[j] <= lim) m = fmaxf(m, sc.tile[i * c + j]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int j = lane; j < c; j += kWave)
+          if (sc.pos[j] <= lim) l += exp2f(sc.tile[i * c + j] - m);
+        l = wave_sum(l);
+        if (lane == 0) {
+          es.qm[i] = m;
+          es.ql[i] = 1.0f / l;
+        }
+      }
+    }
+    __syncthreads();            // tile, positions and window statistics complete
+
+    // scores and keys of the slots.  Thread tid owns slots tid + k*kNT: the
+    // first SPT in registers, any further ones (streams beyond the on-chip
+    // size) as keys in the workspace, each read back only by the thread that
+    // wrote it.
+    int nn = 0, nf = 0;
+    auto score_of = [&](int j, int pj) {
+      float v = 0.f;
+      if (window) {
+#pragma unroll
+        for (int i = 0; i < kMaxWobs; ++i)
+          if (i < W && pj <= t - W + 1 + i) v += exp2f(sc.tile[i * c + j] - es.qm[i]) * es.ql[i];
+      } else {
+        v = (AP && j == slot_new) ? 0.0f : a.score[base + j];
+      }
+      return v;
+    };
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int j = tid + k * kNT;
+      kv[k] = kNone;
+      if (j < c) {
+        const int pj = sc.pos[j];
+        kv[k] = make_skey(sub_of(pj), score_of(j, pj), pj);
+      }
+      const int sb = int(kv[k] >> 62);
+      const uint64_t m0 = __ballot(sb == 0), m1 = __ballot(sb == 1);
+      if (lane == 0) {
+        nn += __popcll(m0);
+        nf += __popcll(m1);
+      }
+    }
+    for (int j = tid + SPT * kNT; j < c; j += kNT) {
+      const int pj = sc.pos[j];
+      const int sb = sub_of(pj);
+      nn += sb == 0;
+      nf += sb == 1;
+      sc.keys[j] = make_skey(sb, score_of(j, pj), pj);
+    }
+    if (c > SPT * kNT) {
+      nn = wave_sum_int(nn);
+      nf = wave_sum_int(nf);
+    }
+    if (lane == 0) {
+      if (nn) atomicAdd(&es.cnt[0], nn);
+      if (nf) atomicAdd(&es.cnt[1], nf);
+    }
+    if (tid < 2 * kNW * kMaxEvict) (&es.cand_key[0][0][0])[tid] = kNone;   // unused entries
+    __syncthreads();            // subset sizes
   }
-  for (int j = tid + SPT * kNT; j < c; j += kNT) {
-    const int pj = sc.pos[j];
-    const int sb = sub_of(pj);
-    nn += sb == 0;
-    nf += sb == 1;
-    sc.keys[j] = make_skey(sb, score_of(j, pj), pj);
-  }
-  if (c > SPT * kNT) {
-    nn = wave_sum_int(nn);
-    nf = wave_sum_int(nf);
-  }
-  if (lane == 0) {
-    if (nn) atomicAdd(&es.cnt[0], nn);
-    if (nf) atomicAdd(&es.cnt[1], nf);
-  }
-  if (tid < 2 * kNW * kMaxEvict) (&es.cand_key[0][0][0])[tid] = kNone;   // unused entries
-  __syncthreads();              // subset sizes
 
   // quotas: floor(M/2) near, the rest far; a short subset gives all it has
   const int E = a.M;
@@ -697,49 +888,29 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
 // present (optional) and, if the stream is a Global stream at B + M slots, evict
 // (optional) — one launch.  Every thread reads the stream's metadata itself
 // (uniform scalar loads, no barrier); the query is requested first.
-template <class T, int D>
-struct StepWaves {
-  static constexpr int value =
-      sizeof(T) == 2 ? (D == 64 ? HKV_WPE_B64 : HKV_WPE_B128) : HKV_WPE_F32;
-};
-template <class T, int D>
-struct StepRows {
-  static constexpr int value = sizeof(T) == 2 ? (D == 64 ? HKV_U_B64 : HKV_U_B128) : HKV_U_F32;
-};
-// Attention of a bf16 Global stream at its eviction point on the matrix cores
-// (one pass yields the output and the W x c scoring tile), or on the vector
-// ALUs like every other stream, the eviction then forming the tile in a second
-// matrix-core pass over K (loaded with caching in the first).  The first keeps
-// the d64 kernel at 6 waves/SIMD; for d128 its registers would cap the whole
-// kernel at 4 waves, the second runs at 5.  Measured on MI355X.
-#ifndef HKV_MFMA_ATTN_B64
-#define HKV_MFMA_ATTN_B64 1
-#endif
-#ifndef HKV_MFMA_ATTN_B128
-#define HKV_MFMA_ATTN_B128 0
-#endif
-template <class T, int D>
-struct StepMfmaAttn {
-  static constexpr bool value =
-      sizeof(T) == 2 && (D == 64 ? HKV_MFMA_ATTN_B64 != 0 : HKV_MFMA_ATTN_B128 != 0);
-};
-
-template <class T, int D, bool AP, bool AT, bool EV>
+template <class T, int D, int C, bool AP, bool AT, bool EV>
 __global__ __launch_bounds__(kNT)
-__attribute__((amdgpu_waves_per_eu(StepWaves<T, D>::value, StepWaves<T, D>::value)))
+__attribute__((amdgpu_waves_per_eu(StepCfg<T, D, C>::kWaves, StepCfg<T, D, C>::kWaves)))
 void k_step(StepArgs a) {
   using F = Frag<T>;
   constexpr int VE = F::N;           // elements per 16-byte fragment
   constexpr int G = D / VE;          // lanes per row
   constexpr int R = kWave / G;       // rows per wave instruction
-  constexpr int U = StepRows<T, D>::value;   // row fragments in flight per lane
+  constexpr int U = StepCfg<T, D, C>::kRows;  // row fragments in flight per lane
   constexpr int ES = sizeof(T);
 
   __shared__ CombineShared cs;
   __shared__ EvictShared es;
-  __shared__ float lds_tile[EV ? kMaxWobs * kLdsSlots : 1];   // W x c floats
-  __shared__ int lds_pos[EV ? kLdsSlots : 1];
-
+  using OC = StepCfg<T, D, C>;
+  // eviction scratch: the W x c tile and positions, or the keys (which also
+  // hold a one-pass tile); positions of a one-pass tile
+  __shared__ float lds_tile[EV && !OC::kKeys ? kMaxWobs * OC::kSlots : 1];
+  __shared__ int lds_pos[EV ? (OC::kKeys ? (OC::kOnePass ? OC::kOnePass : 1) : OC::kSlots) : 1];
+  __shared__ uint64_t lds_keys[EV && OC::kKeys ? OC::kSlots : 1];
+  // window queries of a due bf16 stream whose score tile the eviction computes
+  constexpr bool kQs = EV && sizeof(T) == 2 && !StepMfmaAttn<T, D>::value;
+  static_assert(!kQs || kMaxWobs * D / 4 <= kNT, "one 8-byte query piece per thread");
+  __shared__ __align__(16) uint2 lds_qw[kQs ? kMaxWobs * QStage<D>::kPitch : 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = a.s_begin + xcd_block(blockIdx.x, gridDim.x);
   const int g = lane / G, sub = lane % G;
@@ -748,6 +919,11 @@ void k_step(StepArgs a) {
   // query fragment first: its address does not depend on the stream metadata
   uint4 q_raw = make_uint4(0, 0, 0, 0);
   if (AT) q_raw = ld16_once(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
+  // so is the new token's row (the append's source): threads 0..G-1 take K,
+  // G..2G-1 take V
+  uint4 app = make_uint4(0, 0, 0, 0);
+  if (AP && tid < 2 * G)
+    app = ld16_once((tid >= G ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + (tid % G) * VE) * ES);
 
   // the label byte through the scalar path (aligned 32-bit word), except in a
   // last partial word
@@ -761,7 +937,7 @@ void k_step(StepArgs a) {
   const int B = a.budget[s];
   const long long base = a.base[s];
   const bool glob = lab == HKV_GLOBAL;
-  const int nf0 = glob ? a.n_free[s] : 0;     // freed slots not yet refilled
+  const int nf0 = glob ? a.n_free[s] : 0;    // freed slots not yet refilled
   int ext = ext0, nf = nf0, slot_new = -1;
   bool ok = nf0 >= 0 && nf0 <= a.M;
   if (ok && AP) {
@@ -791,9 +967,22 @@ void k_step(StepArgs a) {
   const bool due = EV && glob && (c == B + a.M);
   // freed slots still empty: the last nf entries of the stream's free list
   int fr[kMaxEvict];
+  static_assert(kMaxEvict <= kWave, "one free-list entry per lane");
+  if constexpr (sizeof(T) == 2 && !kMfma) {
+    // (scalar registers: the d128 kernel's vector registers are the scarce ones)
 #pragma unroll
-  for (int k = 0; k < kMaxEvict; ++k)
-    fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
+    for (int k = 0; k < kMaxEvict; ++k) fr[k] = -1;
+    if (nf > 0) {
+      // one load: lane k fetches entry k, then every entry moves to a scalar register
+      const int frl = lane < nf ? a.free_slots[(long long)s * a.M + (a.M - nf) + lane] : -1;
+#pragma unroll
+      for (int k = 0; k < kMaxEvict; ++k) fr[k] = __builtin_amdgcn_readlane(frl, k);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k)
+      fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
+  }
   auto is_free = [&](int row) {
     bool f = false;
 #pragma unroll
@@ -806,9 +995,8 @@ void k_step(StepArgs a) {
     if (tid < 2 * G) {
       const bool isv = tid >= G;
       const int sb = tid % G;
-      const char* src = (isv ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + sb * VE) * ES;
       char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * D + sb * VE) * ES;
-      st16(dst, ld16_once(src));
+      st16(dst, app);
     }
     if (tid == 0) {
       a.pos[base + slot_new] = a.t;
@@ -816,9 +1004,10 @@ void k_step(StepArgs a) {
     }
   }
 
-  // eviction scratch of a due stream: on chip up to kLdsSlots slots
-  const bool onchip = c <= kLdsSlots;
-  Scratch scr_l{lds_tile, lds_pos, nullptr};
+  // eviction scratch of a due stream: on chip up to the kernel's on-chip size
+  const bool onchip = c <= OC::kSlots;
+  Scratch scr_l{OC::kKeys ? reinterpret_cast<float*>(lds_keys) : lds_tile, lds_pos,
+                OC::kKeys ? lds_keys : nullptr};
   Scratch scr_g{a.ws_tile + base * a.W, a.ws_pos + base, a.ws_keys + base};
   StepCtx x;
   x.base = base;
@@ -866,6 +1055,14 @@ void k_step(StepArgs a) {
     const int t0 = wave * per;
     const int t1 = min(ntiles, t0 + per);
     const bool keep_k = !kMfma && EV && due && a.q_win != nullptr;
+    // the window queries of such a stream are fetched alongside its keys and
+    // staged on chip after the loop
+    const bool stage_q = kQs && keep_k;
+    const int qrow = tid / (D / 4), qcol = tid % (D / 4);
+    uint2 qw_raw = make_uint2(0, 0);
+    if (stage_q && qrow < a.W)
+      qw_raw = *reinterpret_cast<const uint2*>(
+          a.q_win + ((long long)s * a.ld_qw + (long long)qrow * D + qcol * 4) * ES);
 
     float m_run = kNeg, l_run = 0.f;
     float acc[VE];
@@ -923,6 +1120,7 @@ void k_step(StepArgs a) {
       }
       m_run = m_new;
     }
+    if (stage_q && qrow < a.W) lds_qw[qrow * QStage<D>::kPitch + qcol] = qw_raw;
     // combine the R groups of the wave
     const float m_w = cross_group_max<G>(m_run);
     const float f = exp2f(m_run - m_w);
@@ -974,10 +1172,11 @@ void k_step(StepArgs a) {
   if (EV) {
     if (due) {
       const bool ready = tile_here;
+      const bool q_staged = AT && !kMfma && a.q_win != nullptr;   // staged by the attention
       if (onchip)
-        nf_final = evict_stream<T, D, AP>(a, x, scr_l, es, ready);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, ready, lds_qw, q_staged);
       else
-        nf_final = evict_stream<T, D, AP>(a, x, scr_g, es, ready);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, ready, lds_qw, q_staged);
     } else if (a.log && tid < a.M) {
       a.log[(long long)s * a.M + tid] = -1;
     }
@@ -1233,19 +1432,31 @@ hkv_status after_launch(const char* what) {
   return e == hipSuccess ? HKV_OK : hip_fail(e, what);
 }
 
-template <class T, int D, bool AP, bool AT, bool EV>
+template <class T, int D, int C, bool AP, bool AT, bool EV>
 void launch_step_t(const dev::StepArgs& a, int n, hipStream_t st) {
-  hipLaunchKernelGGL((dev::k_step<T, D, AP, AT, EV>), dim3(n), dim3(dev::kNT), 0, st, a);
+  hipLaunchKernelGGL((dev::k_step<T, D, C, AP, AT, EV>), dim3(n), dim3(dev::kNT), 0, st, a);
+}
+
+// Stream class of the bf16 d128 decode step: long streams (the uncompressed
+// layout, or a per-head budget above this many slots) keep more rows in flight
+// per wave; short ones run more waves.  Measured on MI355X.
+#ifndef HKV_LONG_BUDGET
+#define HKV_LONG_BUDGET 192
+#endif
+bool long_streams(const hkv_config* c) {
+  if (c->full_cache) return true;
+  return int64_t(c->rho_num) * c->final_len / c->rho_den > HKV_LONG_BUDGET;
 }
 
 template <bool AP, bool AT, bool EV>
 void launch_step(const hkv_config* c, const dev::StepArgs& a, int n, hipStream_t st) {
   if (c->dtype == HKV_DT_BF16) {
-    if (c->head_dim == 64) launch_step_t<uint16_t, 64, AP, AT, EV>(a, n, st);
-    else launch_step_t<uint16_t, 128, AP, AT, EV>(a, n, st);
+    if (c->head_dim == 64) launch_step_t<uint16_t, 64, 0, AP, AT, EV>(a, n, st);
+    else if (long_streams(c)) launch_step_t<uint16_t, 128, 1, AP, AT, EV>(a, n, st);
+    else launch_step_t<uint16_t, 128, 0, AP, AT, EV>(a, n, st);
   } else {
-    if (c->head_dim == 64) launch_step_t<float, 64, AP, AT, EV>(a, n, st);
-    else launch_step_t<float, 128, AP, AT, EV>(a, n, st);
+    if (c->head_dim == 64) launch_step_t<float, 64, 0, AP, AT, EV>(a, n, st);
+    else launch_step_t<float, 128, 0, AP, AT, EV>(a, n, st);
   }
 }
 
