@@ -229,10 +229,10 @@ struct StepMfmaAttn {
 // (fp32).  Sizes measured on MI355X: the d128 short-stream kernel's LDS stays
 // small enough for 8 workgroups per CU.
 #ifndef HKV_ONCHIP_KEYS
-#define HKV_ONCHIP_KEYS 1024
+#define HKV_ONCHIP_KEYS 1280
 #endif
 #ifndef HKV_ONEPASS_S
-#define HKV_ONEPASS_S 256
+#define HKV_ONEPASS_S 320
 #endif
 #ifndef HKV_ONCHIP_TILE_B16
 #define HKV_ONCHIP_TILE_B16 512

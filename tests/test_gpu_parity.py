@@ -45,18 +45,18 @@ CASES = {
     "long_global": small_config(heads=2, prefix=0, image_tokens=1500, prefill_image=64,
                                 rho=(3, 4), split_dist=300, p_local=0.0),
     # bf16 d128 eviction paths.  Short-stream kernel (per-head budget <= 192):
-    # Global streams of 257..1024 slots (two matrix-core passes, keys on chip;
-    # 3 Global heads of 6, B_g = 288) and beyond 1024 (keys in the workspace;
-    # config id 22 gives 1 Global head of 6, B_g = 1038)
-    "bf16_d128_twopass": small_config(head_dim=128, heads=6, image_tokens=584,
+    # Global streams of 321..1280 slots (two matrix-core passes, keys on chip;
+    # 3 Global heads of 6, B_g = 368) and beyond 1280 (keys in the workspace;
+    # config id 44 gives 1 Global head of 8, B_g = 1436)
+    "bf16_d128_twopass": small_config(head_dim=128, heads=6, image_tokens=744,
                                       prefill_image=100, split_dist=60),
-    "bf16_d128_twopass_spill": small_config(cid=22, head_dim=128, heads=6, image_tokens=1084,
-                                            prefill_image=100, rho=(1, 6), split_dist=60,
-                                            p_local=0.85),
-    # long-stream kernel (budget 225, and 1125 beyond the on-chip keys)
+    "bf16_d128_twopass_spill": small_config(cid=44, head_dim=128, heads=8, image_tokens=1504,
+                                            prefill_image=100, rho=(1, 8), split_dist=60,
+                                            p_local=0.9),
+    # long-stream kernel (budget 225, and 1312 beyond the 1280 on-chip keys)
     "bf16_d128_long": small_config(head_dim=128, heads=2, image_tokens=884, prefill_image=120,
                                    split_dist=80, p_local=0.0),
-    "bf16_d128_long_spill": small_config(head_dim=128, heads=2, prefix=0, image_tokens=1500,
+    "bf16_d128_long_spill": small_config(head_dim=128, heads=2, prefix=0, image_tokens=1750,
                                          prefill_image=64, rho=(3, 4), split_dist=300,
                                          p_local=0.0),
     # ablation variants: eviction without the near/far split; one budget for all
