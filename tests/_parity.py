@@ -69,9 +69,11 @@ def group_streams(w: HkvConfig, groups: Sequence[Tuple[int, int]]) -> List[int]:
 
 
 def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=None,
-                   mode: str = "fused", inputs=None, cache=None) -> GpuRecord:
+                   mode: str = "fused", inputs=None, cache=None,
+                   per_layer: bool = False) -> GpuRecord:
     """Classification and `steps` decode steps over ALL streams, in the layer-
-    folded launch configuration (one call per entry point per step)."""
+    folded launch configuration (one call per entry point per step), or with
+    per_layer one call per layer (its batch x heads streams) as a model runs."""
     K, V, Q = inputs if inputs is not None else device_inputs(w, seed)
     cfg = hk.config_from_workload(w)
     cache = cache or hk.HkvCache(cfg)
@@ -97,7 +99,12 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
         vp = V.data_ptr() + t * d * eb
         qp = Q.data_ptr() + (t - (P - W)) * d * eb          # query of position t
         qw = Q.data_ptr() + (t - W + 1 - (P - W)) * d * eb  # positions t-W+1 .. t
-        if mode == "fused":
+        if mode == "fused" and per_layer:
+            per = w.batch * w.heads
+            for l in range(w.layers):
+                hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log,
+                                   l * per, per)
+        elif mode == "fused":
             hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log, 0, S)
         else:
             hk.hkv_append(cfg, st, t, kp, vp, N * d, 0, S)
