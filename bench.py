@@ -316,6 +316,9 @@ def main():
                     help="also report the attention-output error against the full cache")
     ap.add_argument("--per-layer", action="store_true",
                     help="also time the per-layer decode loop, eager and as a HIP graph")
+    ap.add_argument("--e2e", action="store_true",
+                    help="also time a random-weight transformer of the backbone's shape around "
+                         "the decode path, compressed and full cache (bench_e2e.py)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -394,6 +397,12 @@ def main():
                              "speedup_step": round(ms_f / ms, 3),
                              "speedup_kernel": round(kf / kern_mean_s, 3)}
         del full
+    if args.e2e:
+        import bench_e2e
+        comp = None
+        torch.cuda.empty_cache()
+        res["e2e"] = bench_e2e.run(w, args.seed, max(1, args.steps // 4), hk, device_inputs,
+                                   full_cache_of)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.seed)
     print(json.dumps(res), flush=True)
