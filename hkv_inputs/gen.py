@@ -43,7 +43,7 @@ _W1 = 0xBB67AE85
 _MASK = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
-TAG_K, TAG_V, TAG_QNOISE, TAG_ANCHOR, TAG_BIAS = 0, 1, 2, 3, 4
+TAG_K, TAG_V, TAG_QNOISE, TAG_ANCHOR, TAG_BIAS, TAG_QPRE = 0, 1, 2, 3, 4, 5
 
 
 def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
@@ -225,3 +225,18 @@ def local_flags(cfg: HkvConfig, seed: int) -> np.ndarray:
     """uint8 [S]: 1 where the stream uses the locality-biased query generator."""
     bias = head_bias(cfg, seed)                       # [L, H]
     return np.repeat(bias[:, None, :], cfg.batch, axis=1).reshape(-1).astype(np.uint8)
+
+
+def prefill_queries(cfg: HkvConfig, seed: int) -> np.ndarray:
+    """Bits of the queries of every prefill position, [S, P, d]: positions
+    0 .. P-W-1 standard normal (their own counter tag), the last W positions the
+    workload's observation queries (Q rows 0 .. W-1), so a classification from
+    this prefill sees exactly the observation queries of hkv_classify."""
+    P, W, d = cfg.P, cfg.w_obs, cfg.head_dim
+    out = []
+    _, _, q = all_inputs(cfg, seed)
+    idx = np.arange((P - W) * d, dtype=np.uint64)
+    for s in range(cfg.S):
+        head = encode(normals(cfg, seed, s, TAG_QPRE, idx), cfg.dtype).reshape(P - W, d)
+        out.append(np.concatenate([head, q[s, :W]], axis=0))
+    return np.stack(out)

@@ -73,3 +73,12 @@ def bits_of(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
     return t.detach().cpu().view(torch.int32).numpy().view(np.uint32)
+
+
+def upload_bits(bits: np.ndarray, like: torch.Tensor) -> torch.Tensor:
+    """Device tensor of `like`'s dtype holding the given element bits."""
+    if like.dtype == torch.bfloat16:
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    else:
+        host = torch.from_numpy(np.ascontiguousarray(bits).view(np.float32))
+    return host.to(like.device)

@@ -151,6 +151,20 @@ hkv_status hkv_classify(const hkv_config *cfg, hkv_state *st,
                         const void *k_stage, const void *v_stage, int64_t ld_stage,
                         const void *q_obs, int64_t ld_qobs, void *stream);
 
+/* Steps 1-2 fused into the prefill attention (bf16): the causal attention of
+ * every prefill position over the prefilled cache, written to `out` (stream s
+ * row p at out + s*ld_out + p*head_dim), with the classification of
+ * hkv_classify computed from the same logits, and the initial layout.  The
+ * observation queries are the last W rows of q_stage, so a classification that
+ * only needs the prefill pass (methodology, steps 1 and 2) adds no pass over K.
+ *   q_stage: stream s query of position p at q_stage + s*ld_q + p*head_dim
+ *   k_stage, v_stage: stream s row p at ptr + s*ld_stage + p*head_dim
+ * Same state outputs as hkv_classify; HKV_E_UNSUPPORTED for fp32.  With
+ * full_cache only the attention and the layout are done. */
+hkv_status hkv_prefill(const hkv_config *cfg, hkv_state *st, const void *q_stage,
+                       int64_t ld_q, const void *k_stage, const void *v_stage,
+                       int64_t ld_stage, void *out, int64_t ld_out, void *stream);
+
 /* Append token t (P <= t < N) to every stream of the range: Local slot t mod w;
  * Global: the lowest freed slot if any, else slot `count` (score 0); FULL slot
  * `count`.  k_new/v_new: row of stream s at ptr + s*ld_kv. */

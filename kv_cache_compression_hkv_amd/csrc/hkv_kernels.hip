@@ -1295,6 +1295,207 @@ __global__ __launch_bounds__(kNT) void k_classify(ClassifyArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ k_prefill
+// Causal attention over the P prefill positions of every stream (bf16), with
+// the classification of the compressed layouts as its by-product: the logits of
+// the W observation queries (the last W positions) against every key they see
+// stay on chip, and after the pass the count, label and initial scores follow
+// exactly as in k_classify.  K is read once for both.
+//
+// One workgroup per (stream, block of 64 queries), blocks counted from the end
+// so block 0 holds the observation queries; wave w takes 16 of the block's
+// queries.  The logits are formed transposed on the matrix cores,
+// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys, B = 16 queries):
+// lane l then holds keys (l/16)*4 .. +3 of a 16-key tile for query l%16.  Two
+// such tiles give each lane 8 keys of its query, which is the B operand of
+// O^T += V^T P^T (A = 16 head elements x 32 keys, the same key order), so the
+// probabilities never leave the registers; V is staged transposed in LDS.
+struct PrefillArgs {
+  const char* q_stage; long long ld_q;
+  const char* k_stage; const char* v_stage; long long ld_stage;
+  char* out; long long ld_out;
+  float* init_scores;          // [S, P]
+  int* n_tokens; unsigned char* label;
+  int P, W, w, nqb, classify;
+  float tau, scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int KC = D / 32;                // matrix-core steps over the head elements
+  constexpr int DT = D / 16;                // 16-element output tiles
+  constexpr int BK = 64;                    // keys per block
+  constexpr int VP = BK + 8;                // padded row of the transposed V block
+  constexpr int ES = 2;
+  __shared__ __align__(16) uint16_t vt[D * VP];   // V block, [head element][key]
+  __shared__ float mrow[kMaxWobs], lrow[kMaxWobs];
+  extern __shared__ float lg[];             // [W][P] observation logits (block 0)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const int blk = xcd_block(blockIdx.x, gridDim.x);
+  const int s = blk / a.nqb, qb = blk - (blk / a.nqb) * a.nqb;
+  const int P = a.P, W = a.W;
+  const int q_hi = P - 64 * qb;             // the block's queries: [max(0, q_hi - 64), q_hi)
+  const int myq = q_hi - 64 + 16 * wave + li;
+  const bool qvalid = myq >= 0 && myq < q_hi;
+  const bool obs = a.classify && qb == 0;
+  const long long sb = (long long)s * a.ld_stage;
+
+  // B operand of the logits: query myq, head elements lk*8 + kc*32 .. +7
+  bf16x8 qf[KC];
+  {
+    const int qr = qvalid ? myq : 0;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      uint4 u = ld16(a.q_stage + ((long long)s * a.ld_q + (long long)qr * D + lk * 8 + kc * 32) * ES);
+      if (!qvalid) u = make_uint4(0, 0, 0, 0);
+      qf[kc] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  f32x4 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNeg, l = 0.f;                  // running statistics of query myq
+
+  const int nkb = (q_hi - 1) / BK + 1;      // key blocks the block's queries see
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * BK;
+    __syncthreads();                        // the previous block's V reads are done
+    // V block, transposed: chunk c = 8 elements of key c % 64 (rows past P clamp;
+    // their probabilities are zero)
+    for (int c = tid; c < BK * D / 8; c += kNT) {
+      const int key = c % BK, e0 = (c / BK) * 8;
+      const int kr = min(k0 + key, P - 1);
+      const uint4 v = ld16(a.v_stage + (sb + (long long)kr * D + e0) * ES);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[(e0 + 2 * e) * VP + key] = uint16_t(w4[e] & 0xffffu);
+        vt[(e0 + 2 * e + 1) * VP + key] = uint16_t(w4[e] >> 16);
+      }
+    }
+    // logits of the 4 key tiles: lane holds keys k0 + t*16 + lk*4 + r, query myq
+    float sv[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kr = min(k0 + t * 16 + li, P - 1);
+      uint4 kf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[kc] = ld16(a.k_stage + (sb + (long long)kr * D + lk * 8 + kc * 32) * ES);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kc]), qf[kc],
+                                                      acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = k0 + t * 16 + lk * 4 + r;
+        const bool vis = qvalid && key <= myq;
+        sv[t][r] = vis ? acc[r] * a.scale_log2 : kNeg;
+        if (obs && vis && myq >= P - W) lg[(myq - (P - W)) * P + key] = sv[t][r];
+      }
+    }
+    // online softmax of query myq (its 64 keys sit in the 4 lanes li, li+16, ...)
+    float mb = kNeg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mb = fmaxf(mb, sv[t][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float mn = fmaxf(m, mb);
+    const float alpha = exp2f(m - mn);
+    float pr[4][4], ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[t][r] = sv[t][r] > kNeg ? exp2f(sv[t][r] - mn) : 0.f;
+        ps += pr[t][r];
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    __syncthreads();                        // V block staged
+    // O^T += V^T P^T over 32 keys at a time: keys {2c*16 + lk*4 + e, (2c+1)*16 + lk*4 + e}
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[e] = __bf16(pr[2 * c][e]);
+        pb[4 + e] = __bf16(pr[2 * c + 1][e]);
+      }
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const uint16_t* row = vt + (t * 16 + li) * VP;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + 2 * c * 16 + lk * 4);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + (2 * c + 1) * 16 + lk * 4);
+        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[t],
+                                                       0, 0, 0);
+      }
+    }
+  }
+  // output row myq: head elements t*16 + lk*4 .. +3
+  if (qvalid) {
+    const float inv = 1.0f / l;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out + ((long long)s * a.ld_out + (long long)myq * D) * ES);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      uint2 pk;
+      pk.x = uint32_t(Frag<uint16_t>::from_f32(o[t][0] * inv)) |
+             (uint32_t(Frag<uint16_t>::from_f32(o[t][1] * inv)) << 16);
+      pk.y = uint32_t(Frag<uint16_t>::from_f32(o[t][2] * inv)) |
+             (uint32_t(Frag<uint16_t>::from_f32(o[t][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(orow + t * 16 + lk * 4) = pk;
+    }
+  }
+  if (!obs) return;
+  // ---- classification of the stream, from the observation queries' logits
+  if (qvalid && myq >= P - W && lk == 0) {
+    mrow[myq - (P - W)] = m;
+    lrow[myq - (P - W)] = l;
+  }
+  __syncthreads();
+  // count: attention of the last query accumulated backward from position P-1
+  if (wave == 0) {
+    const int i = W - 1;
+    const float mm = mrow[i], inv = 1.0f / lrow[i];
+    float carry = 0.f;
+    int n = P;
+    for (int d0 = 0; d0 < P; d0 += kWave) {
+      const int dist = d0 + lane;
+      const float p = dist < P ? exp2f(lg[i * P + (P - 1 - dist)] - mm) * inv : 0.f;
+      const float x = wave_inclusive_scan(p, lane) + carry;
+      const uint64_t hit = __ballot(dist < P && x >= a.tau);
+      if (hit) {
+        n = d0 + __ffsll((unsigned long long)hit);   // 1-based lane index = count
+        break;
+      }
+      carry = __shfl(x, 63);
+    }
+    if (lane == 0) {
+      a.n_tokens[s] = n;
+      a.label[s] = n < a.w ? HKV_LOCAL : HKV_GLOBAL;
+    }
+  }
+  // initial scores: column sums of the causal W x P probability tile
+  for (int j = tid; j < P; j += kNT) {
+    float sc = 0.f;
+    for (int i = 0; i < W; ++i)
+      if (j <= P - W + i) sc += exp2f(lg[i * P + j] - mrow[i]) * (1.0f / lrow[i]);
+    a.init_scores[(long long)s * P + j] = sc;
+  }
+}
+
 // ------------------------------------------------------------------ k_layout
 struct LayoutArgs {
   const char* k_stage; const char* v_stage; long long ld_stage;
@@ -1508,9 +1709,12 @@ using namespace hkv;
 
 extern "C" {
 
-hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
-                        const void* v_stage, int64_t ld_stage, const void* q_obs,
-                        int64_t ld_qobs, void* stream) {
+// Classification (k_classify, or k_prefill when q_stage is given, which also
+// writes the prefill attention to `pout`) and initial layout (k_layout).
+static hkv_status classify_impl(const hkv_config* c, hkv_state* st, const void* k_stage,
+                                const void* v_stage, int64_t ld_stage, const void* q_obs,
+                                int64_t ld_qobs, const void* q_stage, int64_t ld_q, void* pout,
+                                int64_t ld_out, void* stream) {
   clear_error();
   Derived d;
   hkv_status r = derive(c, &d);
@@ -1521,7 +1725,17 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
   if ((r = check_data_ptr(v_stage, ld_stage, eb, "v_stage")) != HKV_OK) return r;
   if (ld_stage < int64_t(c->prefill_len) * c->head_dim)
     return fail(HKV_E_INVAL, "ld_stage smaller than prefill_len * head_dim");
-  if (!c->full_cache) {
+  if (q_stage) {
+    if (c->dtype != HKV_DT_BF16)
+      return fail(HKV_E_UNSUPPORTED, "the fused prefill is built for bf16 only");
+    if ((r = check_data_ptr(q_stage, ld_q, eb, "q_stage")) != HKV_OK) return r;
+    if (ld_q < int64_t(c->prefill_len) * c->head_dim)
+      return fail(HKV_E_INVAL, "ld_q smaller than prefill_len * head_dim");
+    if ((r = check_data_ptr(pout, ld_out, eb, "out")) != HKV_OK) return r;
+    if (ld_out < int64_t(c->prefill_len) * c->head_dim)
+      return fail(HKV_E_INVAL, "ld_out smaller than prefill_len * head_dim");
+    if (c->w_obs > 8) return fail(HKV_E_UNSUPPORTED, "classification holds at most 8 queries");
+  } else if (!c->full_cache) {
     if ((r = check_data_ptr(q_obs, ld_qobs, eb, "q_obs")) != HKV_OK) return r;
     if (ld_qobs < int64_t(c->w_obs) * c->head_dim)
       return fail(HKV_E_INVAL, "ld_qobs smaller than w_obs * head_dim");
@@ -1534,7 +1748,33 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
   hipLaunchKernelGGL(dev::k_reset_err, dim3(1), dim3(1), 0, hs, st->err);
   if ((r = after_launch("reset")) != HKV_OK) return r;
 
-  if (!c->full_cache) {
+  if (q_stage) {
+    dev::PrefillArgs a{};
+    a.q_stage = static_cast<const char*>(q_stage);
+    a.ld_q = ld_q;
+    a.k_stage = static_cast<const char*>(k_stage);
+    a.v_stage = static_cast<const char*>(v_stage);
+    a.ld_stage = ld_stage;
+    a.out = static_cast<char*>(pout);
+    a.ld_out = ld_out;
+    a.init_scores = init_scores;
+    a.n_tokens = st->n_tokens;
+    a.label = st->label;
+    a.P = c->prefill_len;
+    a.W = c->w_obs;
+    a.w = c->local_window;
+    a.nqb = (c->prefill_len + 63) / 64;
+    a.classify = c->full_cache ? 0 : 1;
+    a.tau = c->tau;
+    a.scale_log2 = scale_log2_of(c->head_dim);
+    const size_t lds = a.classify ? size_t(c->w_obs) * c->prefill_len * sizeof(float) : 0;
+    const int n = int(d.S) * a.nqb;
+    if (c->head_dim == 64)
+      hipLaunchKernelGGL((dev::k_prefill<64>), dim3(n), dim3(dev::kNT), lds, hs, a);
+    else
+      hipLaunchKernelGGL((dev::k_prefill<128>), dim3(n), dim3(dev::kNT), lds, hs, a);
+    if ((r = after_launch("k_prefill")) != HKV_OK) return r;
+  } else if (!c->full_cache) {
     dev::ClassifyArgs a{};
     a.k_stage = static_cast<const char*>(k_stage);
     a.ld_stage = ld_stage;
@@ -1607,6 +1847,24 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
   if ((r = after_launch("k_layout")) != HKV_OK) return r;
   st->phase = 1;
   return HKV_OK;
+}
+
+hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
+                        const void* v_stage, int64_t ld_stage, const void* q_obs,
+                        int64_t ld_qobs, void* stream) {
+  return classify_impl(c, st, k_stage, v_stage, ld_stage, q_obs, ld_qobs, nullptr, 0, nullptr, 0,
+                       stream);
+}
+
+hkv_status hkv_prefill(const hkv_config* c, hkv_state* st, const void* q_stage, int64_t ld_q,
+                       const void* k_stage, const void* v_stage, int64_t ld_stage, void* out,
+                       int64_t ld_out, void* stream) {
+  if (!q_stage) {
+    clear_error();
+    return fail(HKV_E_INVAL, "q_stage is NULL");
+  }
+  return classify_impl(c, st, k_stage, v_stage, ld_stage, nullptr, 0, q_stage, ld_q, out, ld_out,
+                       stream);
 }
 
 hkv_status hkv_append(const hkv_config* c, hkv_state* st, int32_t t, const void* k_new,

@@ -29,7 +29,7 @@ import kv_cache_compression_hkv_amd as hk
 import oracle.hkv_oracle as O
 from hkv_inputs import gen
 from hkv_inputs.configs import HkvConfig
-from hkv_inputs.gpu import bits_of, device_inputs
+from hkv_inputs.gpu import bits_of, device_inputs, upload_bits
 
 EPS_C = 1e-5
 EPS_S = 1e-5
@@ -70,17 +70,24 @@ def group_streams(w: HkvConfig, groups: Sequence[Tuple[int, int]]) -> List[int]:
 
 def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=None,
                    mode: str = "fused", inputs=None, cache=None,
-                   per_layer: bool = False) -> GpuRecord:
+                   per_layer: bool = False, prefill: bool = False) -> GpuRecord:
     """Classification and `steps` decode steps over ALL streams, in the layer-
     folded launch configuration (one call per entry point per step), or with
-    per_layer one call per layer (its batch x heads streams) as a model runs."""
+    per_layer one call per layer (its batch x heads streams) as a model runs.
+    With prefill the classification comes from hkv_prefill (prefill attention
+    with the classification as a by-product) instead of hkv_classify."""
     K, V, Q = inputs if inputs is not None else device_inputs(w, seed)
     cfg = hk.config_from_workload(w)
     cache = cache or hk.HkvCache(cfg)
     st = cache.state
     S, N, d, P, W, M = w.S, w.N, w.head_dim, w.P, w.w_obs, w.evict_m
     eb = w.elem_bytes
-    hk.hkv_classify(cfg, st, K, V, N * d, Q, w.q_rows * d)
+    if prefill:
+        qs = upload_bits(gen.prefill_queries(w, seed), K)
+        pout = torch.empty((S, P, d), dtype=K.dtype, device=K.device)
+        hk.hkv_prefill(cfg, st, qs, P * d, K, V, N * d, pout, P * d)
+    else:
+        hk.hkv_classify(cfg, st, K, V, N * d, Q, w.q_rows * d)
     idx = torch.tensor(list(streams), dtype=torch.long, device=K.device)
     sl = list(streams)
     lab = cache.label[idx].cpu().numpy()
