@@ -238,6 +238,55 @@ def time_per_layer(gen_obj, steps):
             "capture_s": round(capture_s, 2)}
 
 
+def time_prefill(w, inputs, hk, full_cache_of, reps: int = 5) -> dict:
+    """Classification alone (hkv_classify) against the prefill attention with
+    the classification as its by-product (hkv_prefill), each with the initial
+    layout, on the compressed and on the full-cache layout (where neither
+    classifies, so the difference is the attention alone).  Prefill queries:
+    seeded normal values on the device, the last W rows the workload's
+    observation queries."""
+    import numpy as np
+    import torch
+    K, V, Q = inputs
+    S, P, d, N, W = w.S, w.P, w.head_dim, w.N, w.w_obs
+    g = torch.Generator(device=K.device).manual_seed(7)
+    qs = torch.randn((S, P, d), generator=g, device=K.device).to(K.dtype)
+    qs[:, P - W:] = Q[:, :W]
+    out = torch.empty((S, P, d), dtype=K.dtype, device=K.device)
+    cur = torch.cuda.current_stream()
+
+    def timed(fn):
+        ms = []
+        for k in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            fn()
+            b.record(cur)
+            b.synchronize()
+            if k:
+                ms.append(a.elapsed_time(b))
+        return float(np.mean(ms))
+
+    res = {}
+    for tag, wl in (("compressed", w), ("full_cache", full_cache_of(w))):
+        cfg = hk.config_from_workload(wl)
+        cache = hk.HkvCache(cfg)
+        st = cache.state
+        t_c = timed(lambda: hk.hkv_classify(cfg, st, K, V, N * d, Q, w.q_rows * d, cur))
+        t_p = timed(lambda: hk.hkv_prefill(cfg, st, qs, P * d, K, V, N * d, out, P * d, cur))
+        hk.hkv_check(cfg, st)
+        res[tag] = {"classify_ms": round(t_c, 3), "prefill_ms": round(t_p, 3)}
+        del cache
+        torch.cuda.empty_cache()
+    attn = res["full_cache"]["prefill_ms"] - res["full_cache"]["classify_ms"]
+    byts = 4.0 * S * P * d * K.element_size()          # q, k, v read, output written
+    res["attention_only_ms"] = round(attn, 3)
+    res["fused_extra_ms"] = round(res["compressed"]["prefill_ms"] - res["compressed"]["classify_ms"], 3)
+    res["attention_GBs"] = round(byts / (attn * 1e-3) / 1e9, 1) if attn > 0 else None
+    res["attention_frac"] = round(byts / (attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if attn > 0 else None
+    return res
+
+
 def time_generations(gen_obj, steps, warmup):
     """Mean ms per generation over `steps` timed generations, and the mean
     duration of one decode-step launch (HIP events bracketing each generation's
@@ -316,6 +365,9 @@ def main():
                     help="also report the attention-output error against the full cache")
     ap.add_argument("--per-layer", action="store_true",
                     help="also time the per-layer decode loop, eager and as a HIP graph")
+    ap.add_argument("--prefill", action="store_true",
+                    help="also time hkv_prefill (prefill attention with the classification as "
+                         "its by-product) against hkv_classify")
     ap.add_argument("--e2e", action="store_true",
                     help="also time a random-weight transformer of the backbone's shape around "
                          "the decode path, compressed and full cache (bench_e2e.py)")
@@ -380,6 +432,8 @@ def main():
     }
     if args.per_layer:
         res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2))
+    if args.prefill and w.dtype == "bf16":
+        res["prefill"] = time_prefill(w, inputs, hk, full_cache_of)
     if not args.no_full_cache:
         wf = full_cache_of(w)
         full = Generation(wf, inputs, hk)

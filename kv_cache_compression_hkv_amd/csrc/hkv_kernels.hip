@@ -1309,7 +1309,9 @@ __global__ __launch_bounds__(kNT) void k_classify(ClassifyArgs a) {
 // lane l then holds keys (l/16)*4 .. +3 of a 16-key tile for query l%16.  Two
 // such tiles give each lane 8 keys of its query, which is the B operand of
 // O^T += V^T P^T (A = 16 head elements x 32 keys, the same key order), so the
-// probabilities never leave the registers; V is staged transposed in LDS.
+// probabilities never leave the registers.  Each 64-key block of K and V is
+// staged in LDS once for the four waves (coalesced 16-byte loads; V transposed
+// in registers, 4 keys x 8 elements per thread, and written as 8-byte rows).
 struct PrefillArgs {
   const char* q_stage; long long ld_q;
   const char* k_stage; const char* v_stage; long long ld_stage;
@@ -1329,6 +1331,8 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
   constexpr int BK = 64;                    // keys per block
   constexpr int VP = BK + 8;                // padded row of the transposed V block
   constexpr int ES = 2;
+  constexpr int KP = D + 8;                 // padded row of the K block
+  __shared__ __align__(16) uint16_t ks[BK * KP];  // K block, [key][head element]
   __shared__ __align__(16) uint16_t vt[D * VP];   // V block, [head element][key]
   __shared__ float mrow[kMaxWobs], lrow[kMaxWobs];
   extern __shared__ float lg[];             // [W][P] observation logits (block 0)
@@ -1364,28 +1368,44 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
   for (int kb = 0; kb < nkb; ++kb) {
     const int k0 = kb * BK;
     __syncthreads();                        // the previous block's V reads are done
-    // V block, transposed: chunk c = 8 elements of key c % 64 (rows past P clamp;
-    // their probabilities are zero)
-    for (int c = tid; c < BK * D / 8; c += kNT) {
-      const int key = c % BK, e0 = (c / BK) * 8;
-      const int kr = min(k0 + key, P - 1);
-      const uint4 v = ld16(a.v_stage + (sb + (long long)kr * D + e0) * ES);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    // K block: chunk c = 8 elements (e0) of key c / (D/8); rows past P clamp
+    // (their probabilities are zero)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(e0 + 2 * e) * VP + key] = uint16_t(w4[e] & 0xffffu);
-        vt[(e0 + 2 * e + 1) * VP + key] = uint16_t(w4[e] >> 16);
+    for (int c = tid; c < BK * D / 8; c += kNT) {
+      const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
+      const int kr = min(k0 + key, P - 1);
+      *reinterpret_cast<uint4*>(ks + key * KP + e0) =
+          ld16(a.k_stage + (sb + (long long)kr * D + e0) * ES);
+    }
+    // V block, transposed: patch p = keys 4*(p / (D/8)) .. +3, elements
+    // 8*(p % (D/8)) .. +7, one 8-byte row per element
+    if (tid < BK * D / 32) {
+      const int kg = tid / (D / 8), e0 = (tid % (D / 8)) * 8;
+      uint4 v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = ld16(a.v_stage + (sb + (long long)min(k0 + 4 * kg + i, P - 1) * D + e0) * ES);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = e < 2 ? v[i].x : e < 4 ? v[i].y : e < 6 ? v[i].z : v[i].w;
+          h[i] = (e & 1) ? (w >> 16) : (w & 0xffffu);
+        }
+        *reinterpret_cast<uint2*>(vt + (e0 + e) * VP + 4 * kg) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
       }
     }
+    __syncthreads();                        // K and V blocks staged
     // logits of the 4 key tiles: lane holds keys k0 + t*16 + lk*4 + r, query myq
     float sv[4][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int kr = min(k0 + t * 16 + li, P - 1);
       uint4 kf[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kf[kc] = ld16(a.k_stage + (sb + (long long)kr * D + lk * 8 + kc * 32) * ES);
+        kf[kc] = *reinterpret_cast<const uint4*>(ks + (t * 16 + li) * KP + lk * 8 + kc * 32);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
@@ -1423,7 +1443,6 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
     m = mn;
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] *= alpha;
-    __syncthreads();                        // V block staged
     // O^T += V^T P^T over 32 keys at a time: keys {2c*16 + lk*4 + e, (2c+1)*16 + lk*4 + e}
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
