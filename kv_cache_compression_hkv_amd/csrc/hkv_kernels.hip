@@ -265,9 +265,10 @@ struct QStage {
 
 template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
-                                            EvictShared& es, bool tile_ready, uint2* qs,
-                                            bool q_staged) {
-  // (returns the number of freed slots: M, or 0 if nothing was evicted)
+                                            EvictShared& es, uint64_t* skeys, bool tile_ready,
+                                            uint2* qs, bool q_staged) {
+  // (returns the number of freed slots: M, or 0 if nothing was evicted; skeys:
+  // on-chip room for kNT keys, free once the eviction starts)
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -283,6 +284,10 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   // any further ones are read from the scratch keys
   constexpr int SPT = 2;
   uint64_t kv[SPT];
+  // streams of at most kNT slots are selected by wave 0 alone, over every key:
+  // from the scratch keys when the keys were formed there, else from skeys
+  const bool small = c <= kNT;
+  bool keys_in_scratch = false;
   auto sub_of = [&](int pj) {
     const int dist = t - pj;
     return dist < W ? 2 : (dist < Dd ? 0 : 1);
@@ -297,6 +302,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     // come from the state's scores.
     int nn = 0, nf = 0;                // subset sizes seen by this wave
     const bool one_pass = window && c <= OC::kOnePass;
+    keys_in_scratch = !one_pass;
     if (window) {
       // v_mfma_f32_16x16x32_bf16: A = the W queries (rows W..15 zero), B = 16
       // keys per tile, K = 32 head elements per instruction; lane l holds A row
@@ -431,6 +437,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
           nn += __popcll(__ballot(sb == 0));
           nf += __popcll(__ballot(sb == 1));
         }
+        if (small && tid < c) skeys[tid] = kv[0];
       } else {
         // pass 2: the same logits, now as probabilities summed over each slot's
         // visible queries (rows 0-3 in lanes 0-15, rows 4-7 in lanes 16-31);
@@ -475,7 +482,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     }
     if (tid < 2 * kNW * kMaxEvict) (&es.cand_key[0][0][0])[tid] = kNone;   // unused entries
     __syncthreads();                   // keys and subset sizes
-    if (!one_pass) {
+    if (!one_pass && !small) {
 #pragma unroll
       for (int k = 0; k < SPT; ++k) {
         const int j = tid + k * kNT;
@@ -590,6 +597,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       nn = wave_sum_int(nn);
       nf = wave_sum_int(nf);
     }
+    if (small && tid < c) skeys[tid] = kv[0];
     if (lane == 0) {
       if (nn) atomicAdd(&es.cnt[0], nn);
       if (nf) atomicAdd(&es.cnt[1], nf);
@@ -613,6 +621,60 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     if (tid == 0) atomicOr(a.err, HKV_ERRBIT_SELECT);
     if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
     return 0;
+  }
+
+  if (small) {
+    // wave 0 alone, keys of slots lane + 64*i (i < 4).  Subset 0 keys lie in
+    // [0, 2^62), subset 1 in [2^62, 2^63): each round takes the smallest key of
+    // each subset at or above its lower bound, and the bound moves past it, so
+    // after q rounds a subset's evicted keys are exactly those below its bound.
+    if (wave != 0) return 0;
+    constexpr uint64_t kSub1 = 1ull << 62, kSub2 = 2ull << 62;
+    const uint64_t* src = keys_in_scratch ? sc.keys : skeys;
+    uint64_t k4[kNT / kWave];
+#pragma unroll
+    for (int i = 0; i < kNT / kWave; ++i) {
+      const int j = lane + i * kWave;
+      k4[i] = j < c ? src[j] : kNone;
+    }
+    uint64_t lo0 = 0, lo1 = kSub1;
+    const int qmax = qn > qf ? qn : qf;
+    for (int r = 0; r < qmax; ++r) {
+      uint64_t my0 = kSub1, my1 = kSub2;     // (no key)
+#pragma unroll
+      for (int i = 0; i < kNT / kWave; ++i) {
+        const uint64_t kk = k4[i];
+        if (kk >= lo0 && kk < my0) my0 = kk;
+        if (kk >= lo1 && kk < my1) my1 = kk;
+      }
+      const uint64_t m0 = wave_min_u64(r < qn ? my0 : kSub1);
+      const uint64_t m1 = wave_min_u64(r < qf ? my1 : kSub2);
+      if (m0 < kSub1) lo0 = m0 + 1;
+      if (m1 < kSub2) lo1 = m1 + 1;
+    }
+    // the evicted slots, listed in ascending slot order
+    int ne = 0;
+#pragma unroll
+    for (int i = 0; i < kNT / kWave; ++i) {
+      const uint64_t kk = k4[i];
+      const bool ev = kk < lo0 || (kk >= kSub1 && kk < lo1);
+      const uint64_t bal = __ballot(ev);
+      const int rs = ne + __popcll(bal & ((1ull << lane) - 1));
+      const int j = lane + i * kWave;
+      if (ev && rs < a.M) {
+        a.free_slots[(long long)s * a.M + rs] = j;
+        if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(kk);
+        a.pos[base + j] = -1;
+      }
+      if (a.log && j < c) a.score[base + j] = ev ? 0.0f : skey_score(kk);
+      ne += __popcll(bal);
+    }
+    if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
+    if (ne != a.M) {
+      if (lane == 0) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
+      return 0;
+    }
+    return a.M;
   }
 
   // bottom-q of each subset in two levels.  Every wave takes its own q smallest
@@ -1173,10 +1235,13 @@ void k_step(StepArgs a) {
     if (due) {
       const bool ready = tile_here;
       const bool q_staged = AT && !kMfma && a.q_win != nullptr;   // staged by the attention
+      // the attention's combine buffer is free by now: room for kNT keys
+      static_assert(sizeof(cs.o) >= kNT * sizeof(uint64_t), "combine buffer holds kNT keys");
+      uint64_t* skeys = reinterpret_cast<uint64_t*>(&cs.o[0][0]);
       if (onchip)
-        nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, ready, lds_qw, q_staged);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, skeys, ready, lds_qw, q_staged);
       else
-        nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, ready, lds_qw, q_staged);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, skeys, ready, lds_qw, q_staged);
     } else if (a.log && tid < a.M) {
       a.log[(long long)s * a.M + tid] = -1;
     }
