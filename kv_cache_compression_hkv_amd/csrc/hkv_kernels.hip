@@ -1387,8 +1387,9 @@ struct PrefillArgs {
   float tau, scale_log2;
 };
 
-template <int D>
-__global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
+template <int D, int NWQ>
+__global__ __launch_bounds__(64 * NWQ) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void k_prefill(PrefillArgs a) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   constexpr int KC = D / 32;                // matrix-core steps over the head elements
@@ -1397,6 +1398,8 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
   constexpr int VP = BK + 8;                // padded row of the transposed V block
   constexpr int ES = 2;
   constexpr int KP = D + 8;                 // padded row of the K block
+  constexpr int NT = 64 * NWQ;              // threads; wave w takes queries 16w .. 16w+15
+  constexpr int QB = 16 * NWQ;              // of the workgroup's block of QB queries
   __shared__ __align__(16) uint16_t ks[BK * KP];  // K block, [key][head element]
   __shared__ __align__(16) uint16_t vt[D * VP];   // V block, [head element][key]
   __shared__ float mrow[kMaxWobs], lrow[kMaxWobs];
@@ -1407,8 +1410,9 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
   const int blk = xcd_block(blockIdx.x, gridDim.x);
   const int s = blk / a.nqb, qb = blk - (blk / a.nqb) * a.nqb;
   const int P = a.P, W = a.W;
-  const int q_hi = P - 64 * qb;             // the block's queries: [max(0, q_hi - 64), q_hi)
-  const int myq = q_hi - 64 + 16 * wave + li;
+  const int q_hi = P - QB * qb;             // the block's queries: [max(0, q_hi - QB), q_hi)
+  const int q_w = q_hi - QB + 16 * wave;    // this wave's first query
+  const int myq = q_w + li;
   const bool qvalid = myq >= 0 && myq < q_hi;
   const bool obs = a.classify && qb == 0;
   const long long sb = (long long)s * a.ld_stage;
@@ -1436,7 +1440,7 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
     // K block: chunk c = 8 elements (e0) of key c / (D/8); rows past P clamp
     // (their probabilities are zero)
 #pragma unroll
-    for (int c = tid; c < BK * D / 8; c += kNT) {
+    for (int c = tid; c < BK * D / 8; c += NT) {
       const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
       const int kr = min(k0 + key, P - 1);
       *reinterpret_cast<uint4*>(ks + key * KP + e0) =
@@ -1463,6 +1467,7 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
       }
     }
     __syncthreads();                        // K and V blocks staged
+    if (q_w + 15 < k0) continue;            // (uniform) no query of the wave sees the block
     // logits of the 4 key tiles: lane holds keys k0 + t*16 + lk*4 + r, query myq
     float sv[4][4];
 #pragma unroll
@@ -1572,7 +1577,7 @@ __global__ __launch_bounds__(kNT) void k_prefill(PrefillArgs a) {
     }
   }
   // initial scores: column sums of the causal W x P probability tile
-  for (int j = tid; j < P; j += kNT) {
+  for (int j = tid; j < P; j += NT) {
     float sc = 0.f;
     for (int i = 0; i < W; ++i)
       if (j <= P - W + i) sc += exp2f(lg[i * P + j] - mrow[i]) * (1.0f / lrow[i]);
@@ -1847,16 +1852,27 @@ static hkv_status classify_impl(const hkv_config* c, hkv_state* st, const void* 
     a.P = c->prefill_len;
     a.W = c->w_obs;
     a.w = c->local_window;
-    a.nqb = (c->prefill_len + 63) / 64;
+    // 8 waves (128 queries) per workgroup when one workgroup then covers the
+    // whole prefill: each K and V block is staged once per stream.  Longer
+    // prefills keep 64-query workgroups, which run their key blocks side by
+    // side instead of one after another (measured on MI355X)
+    const int nwq = c->prefill_len > 64 && c->prefill_len <= 128 ? 8 : 4;
+    a.nqb = (c->prefill_len + 16 * nwq - 1) / (16 * nwq);
     a.classify = c->full_cache ? 0 : 1;
     a.tau = c->tau;
     a.scale_log2 = scale_log2_of(c->head_dim);
     const size_t lds = a.classify ? size_t(c->w_obs) * c->prefill_len * sizeof(float) : 0;
     const int n = int(d.S) * a.nqb;
     if (c->head_dim == 64)
-      hipLaunchKernelGGL((dev::k_prefill<64>), dim3(n), dim3(dev::kNT), lds, hs, a);
+      if (nwq == 8)
+        hipLaunchKernelGGL((dev::k_prefill<64, 8>), dim3(n), dim3(512), lds, hs, a);
+      else
+        hipLaunchKernelGGL((dev::k_prefill<64, 4>), dim3(n), dim3(256), lds, hs, a);
     else
-      hipLaunchKernelGGL((dev::k_prefill<128>), dim3(n), dim3(dev::kNT), lds, hs, a);
+      if (nwq == 8)
+        hipLaunchKernelGGL((dev::k_prefill<128, 8>), dim3(n), dim3(512), lds, hs, a);
+      else
+        hipLaunchKernelGGL((dev::k_prefill<128, 4>), dim3(n), dim3(256), lds, hs, a);
     if ((r = after_launch("k_prefill")) != HKV_OK) return r;
   } else if (!c->full_cache) {
     dev::ClassifyArgs a{};
