@@ -59,6 +59,19 @@ CASES = {
     "bf16_d128_long_spill": small_config(head_dim=128, heads=2, prefix=0, image_tokens=1750,
                                          prefill_image=64, rho=(3, 4), split_dist=300,
                                          p_local=0.0),
+    # streams of exactly 256 and 257 slots at eviction (both heads Global,
+    # B_g = 248 and 249): the largest selected by one wave over all keys and the
+    # smallest selected by the per-wave rounds; d64 takes its scores from the
+    # attention's tile, d128 (long-stream kernel) from keys written by its
+    # second matrix-core pass
+    "select_256_d64": small_config(heads=2, prefix=0, image_tokens=496, prefill_image=64,
+                                   rho=(1, 2), split_dist=100, p_local=0.0),
+    "select_257_d64": small_config(heads=2, prefix=0, image_tokens=498, prefill_image=64,
+                                   rho=(1, 2), split_dist=100, p_local=0.0),
+    "select_256_d128": small_config(head_dim=128, heads=2, prefix=0, image_tokens=496,
+                                    prefill_image=64, rho=(1, 2), split_dist=100, p_local=0.0),
+    "select_257_d128": small_config(head_dim=128, heads=2, prefix=0, image_tokens=498,
+                                    prefill_image=64, rho=(1, 2), split_dist=100, p_local=0.0),
     # ablation variants: eviction without the near/far split; one budget for all
     "unstratified": small_config(layers=2, batch=2, unstratified=True),
     "uniform_budget": small_config(rho=(1, 6), split_dist=20, uniform_budget=True),
