@@ -72,6 +72,22 @@ CASES = {
                                     prefill_image=64, rho=(1, 2), split_dist=100, p_local=0.0),
     "select_257_d128": small_config(head_dim=128, heads=2, prefix=0, image_tokens=498,
                                     prefill_image=64, rho=(1, 2), split_dist=100, p_local=0.0),
+    # observation windows W = M other than 8 (quotas 1/1, 2/2, 3/3; fewer window
+    # rows in the matrix-core passes and the staged queries)
+    "window2_d64": small_config(w_obs=2, evict_m=2, heads=4),
+    "window4_d64": small_config(w_obs=4, evict_m=4, layers=2, batch=2),
+    "window6_d64": small_config(w_obs=6, evict_m=6),
+    "window4_d128": small_config(w_obs=4, evict_m=4, head_dim=128, rho=(1, 2), prefill_image=30,
+                                 p_local=0.0),
+    "window6_d128_long": small_config(w_obs=6, evict_m=6, head_dim=128, heads=2, image_tokens=884,
+                                      prefill_image=120, split_dist=80, p_local=0.0),
+    "window4_f32_d128": small_config(w_obs=4, evict_m=4, dtype="f32", head_dim=128, heads=3,
+                                     rho=(1, 6), split_dist=40, p_local=0.0),
+    # W = 4 on streams beyond 256 slots (per-wave rounds) and beyond the on-chip
+    # scratch (workspace)
+    "window4_long_global": small_config(w_obs=4, evict_m=4, heads=2, prefix=0, image_tokens=1500,
+                                        prefill_image=64, rho=(3, 4), split_dist=300,
+                                        p_local=0.0),
     # ablation variants: eviction without the near/far split; one budget for all
     "unstratified": small_config(layers=2, batch=2, unstratified=True),
     "uniform_budget": small_config(rho=(1, 6), split_dist=20, uniform_budget=True),
