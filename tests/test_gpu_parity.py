@@ -83,6 +83,12 @@ CASES = {
                                       prefill_image=120, split_dist=80, p_local=0.0),
     "window4_f32_d128": small_config(w_obs=4, evict_m=4, dtype="f32", head_dim=128, heads=3,
                                      rho=(1, 6), split_dist=40, p_local=0.0),
+    # classification thresholds other than 0.9: mostly Local heads (tau = 0.5),
+    # Global heads needing nearly the whole prefill (tau = 0.99)
+    "tau_half": small_config(tau=0.5, rho=(1, 6), split_dist=20),
+    "tau_099": small_config(tau=0.99, layers=2),
+    # a single decode step after a classification with initial eviction
+    "one_step": small_config(image_tokens=41, prefill_image=40),
     # W = 4 on streams beyond 256 slots (per-wave rounds) and beyond the on-chip
     # scratch (workspace)
     "window4_long_global": small_config(w_obs=4, evict_m=4, heads=2, prefix=0, image_tokens=1500,
