@@ -1434,39 +1434,84 @@ void k_prefill(PrefillArgs a) {
   float m = kNeg, l = 0.f;                  // running statistics of query myq
 
   const int nkb = (q_hi - 1) / BK + 1;      // key blocks the block's queries see
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * BK;
-    __syncthreads();                        // the previous block's V reads are done
-    // K block: chunk c = 8 elements (e0) of key c / (D/8); rows past P clamp
-    // (their probabilities are zero)
+  // K block: chunk c = 8 elements (e0) of key c / (D/8); rows past P clamp
+  // (their probabilities are zero).  V block, transposed: patch p = keys
+  // 4*(p / (D/8)) .. +3, elements 8*(p % (D/8)) .. +7, one 8-byte row per
+  // element.  fetch() loads a block into registers, stage() writes it to LDS.
+  // At d64 the next block is fetched before the current one is used, so its
+  // loads overlap the arithmetic (at d128 the registers would cost a wave).
+  constexpr bool kPF = D == 64;
+  constexpr int KN = (BK * D / 8 + NT - 1) / NT;
+  uint4 kq[kPF ? KN : 1], vq[kPF ? 4 : 1];   // the fetched block (d64)
+  // keys 4*kg .. +3 (rows v[0..3]), elements e0 .. +7 of V, written transposed
+  auto put_v = [&](const uint4* v, int kg, int e0) {
 #pragma unroll
-    for (int c = tid; c < BK * D / 8; c += NT) {
-      const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
-      const int kr = min(k0 + key, P - 1);
-      *reinterpret_cast<uint4*>(ks + key * KP + e0) =
-          ld16(a.k_stage + (sb + (long long)kr * D + e0) * ES);
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = e < 2 ? v[i].x : e < 4 ? v[i].y : e < 6 ? v[i].z : v[i].w;
+        h[i] = (e & 1) ? (w >> 16) : (w & 0xffffu);
+      }
+      *reinterpret_cast<uint2*>(vt + (e0 + e) * VP + 4 * kg) =
+          make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
-    // V block, transposed: patch p = keys 4*(p / (D/8)) .. +3, elements
-    // 8*(p % (D/8)) .. +7, one 8-byte row per element
+  };
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) {
+      const int c = tid + i * NT;
+      if (c < BK * D / 8) {
+        const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
+        kq[i] = ld16(a.k_stage + (sb + (long long)min(k0 + key, P - 1) * D + e0) * ES);
+      }
+    }
     if (tid < BK * D / 32) {
       const int kg = tid / (D / 8), e0 = (tid % (D / 8)) * 8;
-      uint4 v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        v[i] = ld16(a.v_stage + (sb + (long long)min(k0 + 4 * kg + i, P - 1) * D + e0) * ES);
+        vq[i] = ld16(a.v_stage + (sb + (long long)min(k0 + 4 * kg + i, P - 1) * D + e0) * ES);
+    }
+  };
+  auto stage = [&]() {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t h[4];
+    for (int i = 0; i < KN; ++i) {
+      const int c = tid + i * NT;
+      if (c < BK * D / 8) {
+        const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
+        *reinterpret_cast<uint4*>(ks + key * KP + e0) = kq[i];
+      }
+    }
+    if (tid < BK * D / 32) put_v(vq, tid / (D / 8), (tid % (D / 8)) * 8);
+  };
+  if constexpr (kPF) fetch(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int k0 = kb * BK;
+    __syncthreads();                        // the previous block's K and V reads are done
+    if constexpr (kPF) {
+      stage();
+    } else {
+      // (each piece stored as it arrives: fewer registers than fetch + stage)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = e < 2 ? v[i].x : e < 4 ? v[i].y : e < 6 ? v[i].z : v[i].w;
-          h[i] = (e & 1) ? (w >> 16) : (w & 0xffffu);
-        }
-        *reinterpret_cast<uint2*>(vt + (e0 + e) * VP + 4 * kg) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      for (int c = tid; c < BK * D / 8; c += NT) {
+        const int key = c / (D / 8), e0 = (c % (D / 8)) * 8;
+        const int kr = min(k0 + key, P - 1);
+        *reinterpret_cast<uint4*>(ks + key * KP + e0) =
+            ld16(a.k_stage + (sb + (long long)kr * D + e0) * ES);
+      }
+      if (tid < BK * D / 32) {
+        const int kg = tid / (D / 8), e0 = (tid % (D / 8)) * 8;
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] = ld16(a.v_stage + (sb + (long long)min(k0 + 4 * kg + i, P - 1) * D + e0) * ES);
+        put_v(v, kg, e0);
       }
     }
     __syncthreads();                        // K and V blocks staged
+    if constexpr (kPF) {
+      if (kb + 1 < nkb) fetch(k0 + BK);
+    }
     if (q_w + 15 < k0) continue;            // (uniform) no query of the wave sees the block
     // logits of the 4 key tiles: lane holds keys k0 + t*16 + lk*4 + r, query myq
     float sv[4][4];
