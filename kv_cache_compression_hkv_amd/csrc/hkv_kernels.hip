@@ -1727,16 +1727,19 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
       if (lane == 0 && kept != s_B) atomicOr(a.err, HKV_ERRBIT_LAYOUT);
     }
     __syncthreads();
-  } else {
+  } else if (!a.full) {
     for (int j = tid; j < P; j += kNT) {
       if (mode == 1) dest[j] = (j >= P - s_B) ? j % s_B : -1;
       else dest[j] = j;
     }
     __syncthreads();
   }
+  // (the full layout maps position j to slot j; its prefill may exceed the
+  // on-chip table)
+  const bool full = a.full;
   for (int idx = tid; idx < P * 2 * G; idx += kNT) {
     const int j = idx / (2 * G), r = idx % (2 * G);
-    const int to = dest[j];
+    const int to = full ? j : dest[j];
     if (to < 0) continue;
     const bool isv = r >= G;
     const int sub = r % G;
@@ -1744,7 +1747,7 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
     st16((isv ? a.v_pool : a.k_pool) + ((base + to) * D + sub * VE) * ES, ld16(src));
   }
   for (int j = tid; j < P; j += kNT) {
-    const int to = dest[j];
+    const int to = full ? j : dest[j];
     if (to < 0) continue;
     a.pos[base + to] = j;
     a.score[base + to] = (s_lab == HKV_GLOBAL) ? a.init_scores[(long long)s * P + j] : 0.0f;

@@ -38,6 +38,10 @@ CASES = {
     "wide_window": small_config(local_window=44, p_local=1.0),
     # uncompressed baseline layout
     "full_cache": small_config(full_cache=True, image_tokens=120),
+    # uncompressed layout with a prefill beyond the classification's on-chip
+    # limit of 1024 positions (the full layout needs no classification)
+    "full_cache_long_prefill": small_config(full_cache=True, image_tokens=1200,
+                                            prefill_image=1090),
     # odd sizes everywhere
     "ragged": small_config(heads=7, prefix=5, image_tokens=143, prefill_image=37,
                            local_window=13, split_dist=21, rho=(2, 7)),
