@@ -36,6 +36,9 @@ CASES = {
                               rho=(1, 4), split_dist=60),
     "d64_p137_ragged": small_config(heads=5, prefix=5, image_tokens=300, prefill_image=132,
                                     local_window=13, split_dist=21, rho=(2, 7)),
+    # P = 1000, near the classification's limit of 1024 positions: sixteen
+    # query blocks and a 32 KB observation tile on chip
+    "d64_p1000": small_config(heads=2, image_tokens=1100, prefill_image=984),
     # uncompressed layout: attention only
     "d64_full_cache": small_config(full_cache=True, image_tokens=120),
 }
@@ -68,7 +71,8 @@ def test_prefill_outputs(name):
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("name", ["d64_p56", "d128_p116", "d128_p200", "d64_p137_ragged"])
+@pytest.mark.parametrize("name", ["d64_p56", "d128_p116", "d128_p200", "d64_p137_ragged",
+                                  "d64_p1000"])
 def test_prefill_classification_parity(name):
     w = CASES[name]
     print(f"[gpu] prefill classification {name}: S={w.S} P={w.P}", flush=True)
