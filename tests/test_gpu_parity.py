@@ -42,6 +42,9 @@ CASES = {
     # limit of 1024 positions (the full layout needs no classification)
     "full_cache_long_prefill": small_config(full_cache=True, image_tokens=1200,
                                             prefill_image=1090),
+    # a prefill of 1000 positions (classification tile near its 1024 limit) and
+    # an initial eviction of hundreds of tokens (radix select over 1000 keys)
+    "long_prefill": small_config(heads=2, image_tokens=1100, prefill_image=984, p_local=0.0),
     # odd sizes everywhere
     "ragged": small_config(heads=7, prefix=5, image_tokens=143, prefill_image=37,
                            local_window=13, split_dist=21, rho=(2, 7)),
