@@ -51,6 +51,13 @@ CASES = {
     # Global streams longer than the on-chip scratch (spill to the workspace)
     "long_global": small_config(heads=2, prefix=0, image_tokens=1500, prefill_image=64,
                                 rho=(3, 4), split_dist=300, p_local=0.0),
+    # fp32 Global streams beyond the 512-slot on-chip tile (tile, positions and
+    # keys in the workspace), both head sizes
+    "f32_long_global": small_config(dtype="f32", heads=2, prefix=0, image_tokens=1500,
+                                    prefill_image=64, rho=(3, 4), split_dist=300, p_local=0.0),
+    "f32_d128_long_global": small_config(dtype="f32", head_dim=128, heads=2, prefix=0,
+                                         image_tokens=1500, prefill_image=64, rho=(3, 4),
+                                         split_dist=300, p_local=0.0),
     # bf16 d128 eviction paths.  Short-stream kernel (per-head budget <= 192):
     # Global streams of 321..1280 slots (two matrix-core passes, keys on chip;
     # 3 Global heads of 6, B_g = 368) and beyond 1280 (keys in the workspace;
