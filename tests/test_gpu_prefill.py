@@ -39,6 +39,8 @@ CASES = {
     # P = 1000, near the classification's limit of 1024 positions: sixteen
     # query blocks and a 32 KB observation tile on chip
     "d64_p1000": small_config(heads=2, image_tokens=1100, prefill_image=984),
+    # the same at d128: 36 KB of static LDS plus the 32 KB tile
+    "d128_p1000": small_config(head_dim=128, heads=2, image_tokens=1100, prefill_image=984),
     # uncompressed layout: attention only
     "d64_full_cache": small_config(full_cache=True, image_tokens=120),
 }
@@ -72,7 +74,7 @@ def test_prefill_outputs(name):
 
 
 @pytest.mark.parametrize("name", ["d64_p56", "d128_p116", "d128_p200", "d64_p137_ragged",
-                                  "d64_p1000"])
+                                  "d64_p1000", "d128_p1000"])
 def test_prefill_classification_parity(name):
     w = CASES[name]
     print(f"[gpu] prefill classification {name}: S={w.S} P={w.P}", flush=True)
