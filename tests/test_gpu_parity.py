@@ -45,6 +45,8 @@ CASES = {
     # a prefill of 1000 positions (classification tile near its 1024 limit) and
     # an initial eviction of hundreds of tokens (radix select over 1000 keys)
     "long_prefill": small_config(heads=2, image_tokens=1100, prefill_image=984, p_local=0.0),
+    "long_prefill_d128": small_config(head_dim=128, heads=2, image_tokens=1100,
+                                      prefill_image=984, p_local=0.0),
     # odd sizes everywhere
     "ragged": small_config(heads=7, prefix=5, image_tokens=143, prefill_image=37,
                            local_window=13, split_dist=21, rho=(2, 7)),
