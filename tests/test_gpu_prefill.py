@@ -105,3 +105,50 @@ def test_prefill_rejects_f32_and_null():
     with pytest.raises(hk.HkvError):
         hk.hkv_prefill(cfg2, cache2.state, None, w2.P * w2.head_dim, K2, V2, w2.N * w2.head_dim,
                        out, w2.P * w2.head_dim)
+
+
+@pytest.mark.parametrize("name", ["llamagen_xl_rho1_6", "janus_pro_7b_rho1_6"])
+def test_prefill_fullsize(name):
+    """hkv_prefill at a workload's full size, in the launch the benchmark times
+    (queries: seeded normal values on the device, the last W rows the
+    workload's observation queries).  The first and last (layer, sequence)
+    groups are checked against the oracle: every prefill output of every head,
+    and each stream's count and label (a count is flagged, not failed, where
+    tau lies within the oracle's rounding band at the GPU's count)."""
+    from hkv_inputs.configs import WORKLOADS
+    from tests._parity import _count_flag
+    w = WORKLOADS[name]
+    S, P, d, N, W, H = w.S, w.P, w.head_dim, w.N, w.w_obs, w.heads
+    print(f"[gpu] prefill full size {name}: S={S} P={P} d={d}", flush=True)
+    K, V, Q = device_inputs(w, 0)
+    g = torch.Generator(device=K.device).manual_seed(7)
+    qs = torch.randn((S, P, d), generator=g, device=K.device).to(K.dtype)
+    qs[:, P - W:] = Q[:, :W]
+    out = torch.full((S, P, d), float("nan"), dtype=K.dtype, device=K.device)
+    cfg = hk.config_from_workload(w)
+    cache = hk.HkvCache(cfg)
+    hk.hkv_prefill(cfg, cache.state, qs, P * d, K, V, N * d, out, P * d)
+    torch.cuda.synchronize()
+    hk.hkv_check(cfg, cache.state)
+    n_gpu = cache.n_tokens.cpu().numpy()
+    lab_gpu = cache.label.cpu().numpy()
+    err, flagged = 0.0, 0
+    for (l, b) in [(0, 0), (w.layers - 1, w.batch - 1)]:
+        kb, vb, _ = gen.group_inputs(w, 0, l, b)
+        Kf, Vf = gen.decode(kb, w.dtype), gen.decode(vb, w.dtype)
+        for h in range(H):
+            s = w.stream(l, b, h)
+            q = qs[s].float().cpu().numpy().astype(np.float64)
+            o = out[s].float().cpu().numpy()
+            for p in range(P):
+                ref, _ = O.attend(q[p], Kf[h, :p + 1], Vf[h, :p + 1])
+                err = max(err, float(np.abs(o[p] - ref).max()))
+            pr = O.probs(q[P - 1], Kf[h, :P])
+            n_or = O.classify_count(pr, w.tau)
+            if n_or != int(n_gpu[s]):
+                assert _count_flag(pr, int(n_gpu[s]), w.tau), (l, b, h, n_or, int(n_gpu[s]))
+                flagged += 1
+            elif O.label_of(n_or, w.local_window) != int(lab_gpu[s]):
+                raise AssertionError((l, b, h, "label", n_or, int(lab_gpu[s])))
+    print(f"  max abs err {err:.3g}, flagged counts {flagged}", flush=True)
+    assert err <= 2e-2
