@@ -82,3 +82,48 @@ def test_fullsize_variants(unstrat, uniform):
           f"flags {rep.flagged_counts}/{rep.flagged_labels}/{rep.flagged_evictions}", flush=True)
     assert not rep.failures, rep.failures[:8]
     assert rep.events_checked > 0
+
+
+@pytest.mark.parametrize("name", ["llamagen_xl_rho1_6", "janus_pro_1b_rho1_4"])
+def test_fullsize_per_layer_equals_folded(name):
+    """One launch per layer per step (a model's loop) against one launch over
+    all layers per step, at full size: each stream's work does not depend on
+    which launch carries it, so every output of every step and the final
+    state agree bit for bit."""
+    import bench
+    import kv_cache_compression_hkv_amd as hk
+    from hkv_inputs.gpu import device_inputs
+    w = WORKLOADS[name]
+    print(f"[gpu] per-layer vs folded {name}: S={w.S} steps={w.steps}", flush=True)
+    inputs = device_inputs(w, SEED)
+    d, per, W = w.head_dim, w.batch * w.heads, w.w_obs
+    cur = torch.cuda.current_stream()
+
+    def state(g):
+        c = g.cache
+        return [t.clone() for t in (c.pos, c.count, c.n_free, c.free_slots, c.label, c.budget)]
+
+    folded = bench.Generation(w, inputs, hk)
+    cap_f = torch.empty((w.steps, w.S, d), dtype=folded.out.dtype, device=folded.out.device)
+    folded.run(cur, capture=cap_f)
+    torch.cuda.synchronize()
+    hk.hkv_check(folded.cfg, folded.cache.state)
+    st_f = state(folded)
+    del folded
+
+    layered = bench.Generation(w, inputs, hk)
+    st = layered.cache.state
+    hk.hkv_classify(layered.cfg, st, layered.K, layered.V, w.N * d, layered.Q, w.q_rows * d, cur)
+    cap_l = torch.empty_like(cap_f)
+    for t in range(w.P, w.N):
+        for l in range(w.layers):
+            hk.hkv_decode_step(layered.cfg, st, t, layered.kp[t], layered.vp[t], w.N * d,
+                               layered.qw[t], w.q_rows * d, layered.out, d, None, l * per, per,
+                               cur)
+        cap_l[t - w.P].copy_(layered.out)
+    torch.cuda.synchronize()
+    hk.hkv_check(layered.cfg, st)
+    st_l = state(layered)
+    assert torch.equal(cap_f.view(torch.int16), cap_l.view(torch.int16))
+    for a, b in zip(st_f, st_l):
+        assert torch.equal(a, b)
