@@ -297,17 +297,40 @@ def time_generations(gen_obj, steps, warmup):
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         gen_obj.run(stream)
+        gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state, stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         gen_obj.run(stream, evs[k])
+        # every generation's classification clears the device error word, so
+        # each one is checked before the next starts
+        gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     loop_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
     return wall / steps * 1e3, loop_ms / gen_obj.w.steps
+
+
+def measure(w, inputs, hk, steps, warmup):
+    """Timed generations of one workload: tokens/s over the whole generation
+    and the dominant kernel's roofline figures (algorithmic bytes per launch /
+    mean launch time from HIP events on the launch stream)."""
+    gen_obj = Generation(w, inputs, hk)
+    ms, launch_ms = time_generations(gen_obj, steps, warmup)
+    labels = gen_obj.cache.label.cpu().numpy()
+    budgets = gen_obj.cache.budget.cpu().numpy()
+    alg = step_bytes(labels, budgets, w)
+    kern_s = float(launch_ms.mean()) * 1e-3
+    achieved = float(alg.mean()) / kern_s / 1e9
+    return gen_obj, {"value": round(w.batch * w.steps / (ms * 1e-3), 1), "unit": "tokens/s",
+                     "ms_per_step": round(ms, 4), "mean_launch_us": round(kern_s * 1e6, 3),
+                     "alg_bytes_per_launch": round(float(alg.mean()), 1),
+                     "achieved_GBs": round(achieved, 1),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "labels": {"local": int((labels == 0).sum()),
+                                "global": int((labels == 1).sum())}}
 
 
 def fidelity(comp, full):
@@ -354,6 +377,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llamagen_xl_rho1_6")
+    ap.add_argument("--second", default="janus_pro_7b_rho1_6",
+                    help="a second workload measured the same way in the same run "
+                         "(compressed layout only; '' to skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-cache", action="store_true")
@@ -394,15 +420,12 @@ def main():
     torch.cuda.set_device(0)
     inputs = device_inputs(w, args.seed)
 
-    comp = Generation(w, inputs, hk)
-    ms, launch_ms = time_generations(comp, args.steps, args.warmup)
-    labels = comp.cache.label.cpu().numpy()
-    budgets = comp.cache.budget.cpu().numpy()
-    alg = step_bytes(labels, budgets, w)                     # [T]
-    kern_mean_s = float(launch_ms.mean()) * 1e-3
-    achieved = float(alg.mean()) / kern_mean_s / 1e9         # GB/s
+    comp, m = measure(w, inputs, hk, args.steps, args.warmup)
+    ms = m["ms_per_step"]
+    kern_mean_s = m["mean_launch_us"] * 1e-6
+    achieved = m["achieved_GBs"]
     tokens = w.batch * w.steps
-    value = tokens / (ms * 1e-3)
+    value = m["value"]
 
     traffic = None
     if os.path.exists(COUNTERS_FILE):
@@ -422,13 +445,13 @@ def main():
                    "launch": "layer-folded, 1 fused launch per decode step",
                    "variant": args.variant,
                    "global_batch": w.batch, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": m["frac"],
                      "traffic": traffic,
                      "kernel": "k_step (fused append + attention + STE)",
-                     "mean_launch_us": round(kern_mean_s * 1e6, 3),
-                     "alg_bytes_per_launch": round(float(alg.mean()), 1)},
-        "labels": {"local": int((labels == 0).sum()), "global": int((labels == 1).sum())},
+                     "mean_launch_us": m["mean_launch_us"],
+                     "alg_bytes_per_launch": m["alg_bytes_per_launch"]},
+        "labels": m["labels"],
     }
     if args.per_layer:
         res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2))
@@ -451,6 +474,20 @@ def main():
                              "speedup_step": round(ms_f / ms, 3),
                              "speedup_kernel": round(kf / kern_mean_s, 3)}
         del full
+    if args.second and args.second != w.name:
+        # the second rho = 1/6 workload, same protocol (compressed layout only)
+        comp = None
+        torch.cuda.empty_cache()
+        w2 = WORKLOADS[args.second]
+        if args.variant != "headkv":
+            w2 = variant_of(w2, *VARIANTS[args.variant])
+        inputs2 = device_inputs(w2, args.seed)
+        g2, m2 = measure(w2, inputs2, hk, args.steps, args.warmup)
+        m2["workload"] = w2.name
+        m2["rho"] = f"{w2.rho[0]}/{w2.rho[1]}"
+        res["second_workload"] = m2
+        del g2, inputs2
+        torch.cuda.empty_cache()
     if args.e2e:
         import bench_e2e
         comp = None

@@ -165,15 +165,32 @@ hkv_status hkv_prefill(const hkv_config *cfg, hkv_state *st, const void *q_stage
                        int64_t ld_q, const void *k_stage, const void *v_stage,
                        int64_t ld_stage, void *out, int64_t ld_out, void *stream);
 
-/* Append token t (P <= t < N) to every stream of the range: Local slot t mod w;
- * Global: the lowest freed slot if any, else slot `count` (score 0); FULL slot
- * `count`.  k_new/v_new: row of stream s at ptr + s*ld_kv. */
+/* Append token t (P <= t < N) to every stream of the range.
+ * Pages: section "Methodology", step 3 — a Local head's sliding window takes the
+ * newest token and drops the oldest; a Global head's cache takes every new
+ * token until its budget forces an eviction (the append itself is implicit on
+ * the pages).
+ * Local: slot t mod w (ring; the uniform-budget variant: t mod A); Global: the
+ * lowest freed slot if any, else slot `count`, with score 0; FULL: slot
+ * `count`.  k_new/v_new: device rows of stream s at ptr + s*ld_kv (elements),
+ * 16-byte aligned, read only.  Errors: HKV_E_STATE before classification,
+ * HKV_E_INVAL for a bad t, range or pointer; appending to a full Global or FULL
+ * stream sets HKV_ERRBIT_CAPACITY on the device (hkv_check). */
 hkv_status hkv_append(const hkv_config *cfg, hkv_state *st, int32_t t,
                       const void *k_new, const void *v_new, int64_t ld_kv,
                       int32_t s_begin, int32_t s_count, void *stream);
 
 /* Decode attention at step t over the slots present (the cache already holds
- * token t): out row of stream s at out + s*ld_o, q row at q + s*ld_q. */
+ * token t).
+ * Pages: section "Methodology", step 3 — a Local head attends only to its
+ * sliding window of the newest tokens, a Global head to the tokens its
+ * Stratified Token Eviction has kept; the problem definition names the KV
+ * cache read of this step as what limits decoding.
+ * o = sum_j softmax_j(q.k_j / sqrt(d)) v_j over the stream's live slots, fp32
+ * arithmetic, rounded to the element type.  q: device row of stream s at
+ * q + s*ld_q; out: device row at out + s*ld_o (written, 4-byte aligned).  The
+ * state is read only.  Errors: HKV_E_STATE before classification, HKV_E_INVAL
+ * for a bad t, range or pointer. */
 hkv_status hkv_decode_attn(const hkv_config *cfg, hkv_state *st, int32_t t,
                            const void *q, int64_t ld_q, void *out, int64_t ld_o,
                            int32_t s_begin, int32_t s_count, void *stream);
@@ -181,6 +198,11 @@ hkv_status hkv_decode_attn(const hkv_config *cfg, hkv_state *st, int32_t t,
 /* STE at step t for every Global stream of the range holding budget + M
  * tokens: score the slots, evict M (floor(M/2) near, the rest far) and free
  * their slots (free_slots, n_free = M; no row moves).
+ * Pages: section "Methodology", step 3, Global heads — Stratified Token
+ * Eviction splits the candidate past tokens by distance into disjoint near and
+ * far subsets, scores each subset on its own from past query features and
+ * evicts the lowest-scoring tokens of each (M/2 + M/2); section "Key
+ * contributions", item 3, for why the split keeps distant tokens.
  *   q_win: the W most recent queries (positions t-W+1 .. t, oldest first) of
  *          stream s at q_win + s*ld_qw + r*head_dim.  A slot's score is the sum
  *          over these queries of the softmax probability it receives, each query
@@ -189,15 +211,24 @@ hkv_status hkv_decode_attn(const hkv_config *cfg, hkv_state *st, int32_t t,
  *          NULL: the scores are taken from st->score as stored by the caller.
  *   evicted_pos_log (optional, device, [S, M] int32): evicted positions in
  *          ascending slot order, -1 for streams that did not evict.
- * With a log, an eviction also writes the scores of every slot to st->score
- * (0 for the freed ones). */
+ * With a log, an eviction also writes the score of every slot it ranked to
+ * st->score, the evicted ones included (a freed slot's score is reset to 0 when
+ * a token refills it).  Errors: HKV_E_STATE before classification, HKV_E_INVAL
+ * for a bad t, range or pointer; too few candidates sets HKV_ERRBIT_SELECT on
+ * the device (hkv_check). */
 hkv_status hkv_ste_evict(const hkv_config *cfg, hkv_state *st, int32_t t,
                          const void *q_win, int64_t ld_qw, int32_t *evicted_pos_log,
                          int32_t s_begin, int32_t s_count, void *stream);
 
 /* One decode step in a single launch: exactly hkv_append, then hkv_decode_attn
  * with the newest query of the window (row W-1), then hkv_ste_evict with the
- * window, with identical results (bit for bit). */
+ * window, with identical results (bit for bit).
+ * Pages: section "Methodology", step 3 — the whole per-token work of the
+ * compressed decode: the Local sliding window or the Global cache takes the new
+ * token, the head attends over what it keeps, and a Global head at its budget
+ * runs Stratified Token Eviction.  Arguments, layouts and errors are those of
+ * the three calls; k_new/v_new rows at ptr + s*ld_kv, the W-query window at
+ * q_win + s*ld_qw (oldest first), out at out + s*ld_o. */
 hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
                            const void *k_new, const void *v_new, int64_t ld_kv,
                            const void *q_win, int64_t ld_qw, void *out, int64_t ld_o,

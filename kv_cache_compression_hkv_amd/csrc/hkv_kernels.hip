@@ -120,12 +120,10 @@ struct CombineShared {
 
 struct EvictShared {
   int cnt[2];
-  int ne;
   float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / 1/sum of each window query
   float pm[kNW][kMaxWobs], pl[kNW][kMaxWobs];   // per-wave partials of the tile pass
   uint64_t cand_key[2][kNW][kMaxEvict];  // per subset and wave: its bottom-q keys
   int cand_slot[2][kNW][kMaxEvict];
-  int ev_slot[kMaxEvict];              // evicted slots in ascending order
 };
 
 // Eviction key with the subset in the top bits: (subset << 62) | (score bits <<
@@ -465,6 +463,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         });
       }
     } else {
+      __syncthreads();                 // subset counters zeroed before any wave adds
       for (int j0 = wave * kWave; j0 < c; j0 += kNT) {
         const int j = j0 + lane;
         const bool own = j < c;
@@ -666,7 +665,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(kk);
         a.pos[base + j] = -1;
       }
-      if (a.log && j < c) a.score[base + j] = ev ? 0.0f : skey_score(kk);
+      if (a.log && j < c) a.score[base + j] = skey_score(kk);
       ne += __popcll(bal);
     }
     if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
@@ -749,28 +748,19 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       a.free_slots[(long long)s * a.M + rs] = j;
       if (a.log) a.log[(long long)s * a.M + rs] = skey_pos(mine);
       a.pos[base + j] = -1;
-      es.ev_slot[rs] = j;
     }
     if (a.log && lane < a.M && lane >= ne) a.log[(long long)s * a.M + lane] = -1;
-    if (lane == 0) es.ne = ne;
     ne_all = ne;
   }
-  // with a log, the scores of the event (0 for the freed slots)
+  // with a log, the scores the event ranked (every slot, the evicted ones
+  // included; the append that refills a freed slot resets its score)
   if (a.log) {
-    __syncthreads();            // freed slots listed
-    const int ne = es.ne;
-    auto freed = [&](int j) {
-      bool f = false;
-      for (int m = 0; m < ne && m < a.M; ++m) f |= es.ev_slot[m] == j;
-      return f;
-    };
 #pragma unroll
     for (int k = 0; k < SPT; ++k) {
       const int j = tid + k * kNT;
-      if (j < c) a.score[base + j] = freed(j) ? 0.0f : skey_score(kv[k]);
+      if (j < c) a.score[base + j] = skey_score(kv[k]);
     }
-    for (int j = tid + SPT * kNT; j < c; j += kNT)
-      a.score[base + j] = freed(j) ? 0.0f : skey_score(sc.keys[j]);
+    for (int j = tid + SPT * kNT; j < c; j += kNT) a.score[base + j] = skey_score(sc.keys[j]);
   }
   // (only wave 0's value is used: the epilogue runs on thread 0)
   if (ne_all != a.M) {

@@ -2,8 +2,9 @@
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
 this module.  The product (the native library and its binding) never calls it,
-and it shares no code with that product: it imports numpy and the seeded input
-module (``hkv_inputs``, which holds no method arithmetic) and nothing else.
+and it shares no code with that product: it imports numpy and the Python
+standard library and nothing else.  Its callers hand it inputs decoded from the
+seeded input module ``hkv_inputs``, which holds no method arithmetic.
 
 Everything is plain float64 numpy, one stream and one step at a time, following
 the method's steps in the order the pages give them.  Citations name the pages
@@ -183,7 +184,8 @@ def window_scores(Qwin: np.ndarray, K: np.ndarray, first_pos: int) -> np.ndarray
     """Importance of every prefill position from the w_obs last prefill queries:
     query at position i (i = first_pos .. first_pos + W - 1) attends causally to
     positions 0..i; the score of position j is the sum of the probabilities it
-    receives (reading of 'scored from past query features')."""
+    receives (reading of 'scored from past query features', [Method/3G], applied
+    when the cache reaches its predefined length, [Method/2])."""
     P = first_pos + Qwin.shape[0]
     score = np.zeros(P)
     for r, q in enumerate(Qwin):

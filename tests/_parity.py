@@ -52,6 +52,9 @@ class GpuRecord:
     count_final: np.ndarray
     tables_final: List[List[int]]
     scores_final: List[np.ndarray]
+    scores0: List[np.ndarray]                  # scores after classification
+    score_trace: Optional[np.ndarray] = None   # [T, sum of caps]: scores after each step
+    score_off: Optional[List[int]] = None      # column of each stream's first slot
 
 
 def _tables(cache: hk.HkvCache, streams, counts) -> List[List[int]]:
@@ -70,12 +73,16 @@ def group_streams(w: HkvConfig, groups: Sequence[Tuple[int, int]]) -> List[int]:
 
 def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=None,
                    mode: str = "fused", inputs=None, cache=None,
-                   per_layer: bool = False, prefill: bool = False) -> GpuRecord:
+                   per_layer: bool = False, prefill: bool = False,
+                   score_trace: bool = False) -> GpuRecord:
     """Classification and `steps` decode steps over ALL streams, in the layer-
     folded launch configuration (one call per entry point per step), or with
     per_layer one call per layer (its batch x heads streams) as a model runs.
     With prefill the classification comes from hkv_prefill (prefill attention
-    with the classification as a by-product) instead of hkv_classify."""
+    with the classification as a by-product) instead of hkv_classify.  With
+    score_trace the scores of the recorded streams' slots are read back after
+    every step (an eviction writes the scores it ranked when given a log), for
+    a comparison at every eviction event."""
     K, V, Q = inputs if inputs is not None else device_inputs(w, seed)
     cfg = hk.config_from_workload(w)
     cache = cache or hk.HkvCache(cfg)
@@ -92,10 +99,23 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
     sl = list(streams)
     lab = cache.label[idx].cpu().numpy()
     cnt0 = cache.count[idx].cpu().numpy()
+    base0 = cache.base.cpu().numpy()
+    capv = cache.cap[idx].cpu().numpy()
     rec = dict(streams=sl, labels=lab, n_tokens=cache.n_tokens[idx].cpu().numpy(),
-               budget=cache.budget[idx].cpu().numpy(), cap=cache.cap[idx].cpu().numpy(),
-               count0=cnt0, tables0=_tables(cache, sl, cnt0))
+               budget=cache.budget[idx].cpu().numpy(), cap=capv,
+               count0=cnt0, tables0=_tables(cache, sl, cnt0),
+               scores0=[cache.score[int(base0[s]):int(base0[s]) + int(c)].cpu().numpy()
+                        for s, c in zip(sl, cnt0)])
     T = w.steps if steps is None else steps
+    trace = None
+    if score_trace:
+        offs, cols = [], []
+        for s, c in zip(sl, capv):
+            offs.append(sum(len(x) for x in cols))
+            cols.append(torch.arange(int(base0[s]), int(base0[s]) + int(c), dtype=torch.long))
+        sidx = torch.cat(cols).to(K.device)
+        trace = torch.empty((T, sidx.numel()), dtype=torch.float32, device=K.device)
+        rec["score_off"] = offs
     out = torch.zeros((S, d), dtype=K.dtype, device=K.device)
     log = torch.full((S, M), -1, dtype=torch.int32, device=K.device)
     outs = torch.empty((T, len(sl), d), dtype=K.dtype, device=K.device)
@@ -119,7 +139,11 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
             hk.hkv_ste_evict(cfg, st, t, qw, w.q_rows * d, log, 0, S)
         outs[step] = out[idx]
         logs[step] = log[idx]
+        if trace is not None:
+            trace[step] = cache.score[sidx]
     hk.hkv_check(cfg, st)
+    if trace is not None:
+        rec["score_trace"] = trace.cpu().numpy()
     cntf = cache.count[idx].cpu().numpy()
     rec.update(outs=gen.decode(bits_of(outs), w.dtype), logs=logs.cpu().numpy(),
                count_final=cntf, tables_final=_tables(cache, sl, cntf))
@@ -137,6 +161,7 @@ class Report:
     flagged_labels: int = 0
     flagged_evictions: int = 0
     events_checked: int = 0
+    lockstep_events: int = 0     # events whose GPU scores were compared one by one
     outputs_checked: int = 0
     max_out_err: float = 0.0
     max_score_err: float = 0.0
@@ -209,6 +234,30 @@ def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
             if int(g.labels[gi[h]]) != O.FULL:
                 rep.fail(f"h{h}: full-cache label {g.labels[gi[h]]}")
 
+    def lockstep(h, t, slot_pos, slot_score, gpu):
+        """The GPU's own scores at this event: each within EPS_S of the oracle's,
+        and the oracle's selection run on them gives the GPU's evicted set."""
+        c = gi[h]
+        if t == P - 1:                  # kept positions, in the order of the table
+            got = np.asarray(g.scores0[c], dtype=np.float64)
+            want = np.asarray([slot_score[p] for p in g.tables0[c]])
+        else:
+            if g.score_trace is None:
+                return
+            o = g.score_off[c]
+            got = g.score_trace[t - P, o:o + len(slot_pos)].astype(np.float64)
+            want = np.asarray(slot_score, dtype=np.float64)
+            again = O.ste_select(slot_pos, got, t, W, D, len(gpu))
+            if again != gpu:
+                rep.fail(f"l{l} b{b} h{h} t{t}: selection on the GPU's scores "
+                         f"{[slot_pos[j] for j in again]} != its evicted set "
+                         f"{[slot_pos[j] for j in gpu]}")
+        err = float(np.max(np.abs(got - want))) if got.size else 0.0
+        rep.max_score_err = max(rep.max_score_err, err)
+        if err > EPS_S:
+            rep.fail(f"l{l} b{b} h{h} t{t}: GPU scores differ by {err:.3g}")
+        rep.lockstep_events += 1
+
     def hook(h, t, slot_pos, slot_score, own):
         if t == P - 1:
             kept = set(g.tables0[gi[h]])
@@ -217,6 +266,7 @@ def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
             row = g.logs[t - P, gi[h]]
             gpu_pos = {int(x) for x in row if x >= 0}
         gpu = sorted(j for j in range(len(slot_pos)) if slot_pos[j] in gpu_pos)
+        lockstep(h, t, slot_pos, slot_score, gpu)
         rep.events_checked += 1
         if gpu == own:
             return None
@@ -246,12 +296,14 @@ def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
             tf = [p for p in tf[:int(g.count_final[c])]]
         if tf != g.tables_final[c]:
             rep.fail(f"l{l} b{b} h{h}: final layout differs")
-        # scores written at the stream's last eviction (0 for freed slots; slots
-        # refilled after it were reset to 0 by their append)
+        # scores written at the stream's last eviction (every ranked slot, the
+        # evicted ones included; slots refilled after it were reset to 0 by their
+        # append)
         evs = [ev for ev in rec.events if ev.head == h]
         if evs and lab == O.GLOBAL:
             ev = evs[-1]
-            _, want, _ = O.free_evicted(ev.slot_pos, ev.slot_score, ev.evicted_slots)
+            want = [0.0 if (j in ev.evicted_slots and rec.tables_final[h][j] >= 0) else x
+                    for j, x in enumerate(ev.slot_score)]
             got_sc = np.asarray(g.scores_final[c][:len(want)], dtype=np.float64)
             err = float(np.max(np.abs(got_sc - np.asarray(want)))) if len(want) else 0.0
             rep.max_score_err = max(rep.max_score_err, err)

@@ -110,6 +110,16 @@ CASES = {
     "window4_long_global": small_config(w_obs=4, evict_m=4, heads=2, prefix=0, image_tokens=1500,
                                         prefill_image=64, rho=(3, 4), split_dist=300,
                                         p_local=0.0),
+    # local window longer than the prefill: every head is Local (its count is at
+    # most P < w) and its ring starts part-filled, then grows to w
+    "window_gt_prefill": small_config(local_window=64, rho=(1, 2)),
+    "window_gt_prefill_f32_d128": small_config(dtype="f32", head_dim=128, heads=3,
+                                               local_window=70, rho=(1, 2)),
+    # uniform budget with floor(rho*N) above the prefill: Local rings of A slots
+    # start part-filled; Global heads grow from P to A before their first eviction
+    "uniform_ring_gt_prefill": small_config(rho=(1, 2), uniform_budget=True),
+    "uniform_ring_gt_prefill_d128": small_config(head_dim=128, rho=(1, 2), tau=0.5,
+                                                 uniform_budget=True),
     # ablation variants: eviction without the near/far split; one budget for all
     "unstratified": small_config(layers=2, batch=2, unstratified=True),
     "uniform_budget": small_config(rho=(1, 6), split_dist=20, uniform_budget=True),
@@ -123,22 +133,57 @@ def _all_groups(w):
     return [(l, b) for l in range(w.layers) for b in range(w.batch)]
 
 
-@pytest.mark.parametrize("name", ["tiny"] + sorted(CASES))
-def test_parity_small(name):
-    w = TINY if name == "tiny" else CASES[name]
-    print(f"[gpu] parity {name}: S={w.S} N={w.N} P={w.P} d={w.head_dim} {w.dtype}", flush=True)
+NO_EVENTS = ("rho_one", "wide_window", "window_gt_prefill", "window_gt_prefill_f32_d128")
+
+
+def _check_all_groups(w, name, **kw):
+    """Every group of a small workload, every step; the GPU's scores compared
+    with the oracle's at every eviction event (lock-step)."""
     groups = _all_groups(w)
-    g = gpu_generation(w, 0, group_streams(w, groups))
+    g = gpu_generation(w, 0, group_streams(w, groups), score_trace=True, **kw)
     rep = None
     for (l, b) in groups:
         rep = oracle_check_group(w, 0, l, b, g, rep=rep)
     print(f"  outputs {rep.outputs_checked} events {rep.events_checked} "
-          f"max err {rep.max_out_err:.3g} score err {rep.max_score_err:.3g} "
-          f"flags {rep.flagged_counts}/{rep.flagged_labels}/"
-          f"{rep.flagged_evictions}", flush=True)
+          f"(lock-step {rep.lockstep_events}) max err {rep.max_out_err:.3g} "
+          f"score err {rep.max_score_err:.3g} flags {rep.flagged_counts}/"
+          f"{rep.flagged_labels}/{rep.flagged_evictions}", flush=True)
     assert not rep.failures, rep.failures[:8]
-    if name not in ("rho_one", "wide_window") and not w.full_cache:
+    if name not in NO_EVENTS and not w.full_cache:
         assert rep.events_checked > 0
+        assert rep.lockstep_events == rep.events_checked
+    # deterministic inputs: no decision of these cases falls inside a flag band
+    assert rep.flagged_counts == rep.flagged_labels == rep.flagged_evictions == 0
+    return g, rep
+
+
+@pytest.mark.parametrize("name", ["tiny"] + sorted(CASES))
+def test_parity_small(name):
+    w = TINY if name == "tiny" else CASES[name]
+    print(f"[gpu] parity {name}: S={w.S} N={w.N} P={w.P} d={w.head_dim} {w.dtype}", flush=True)
+    g, _ = _check_all_groups(w, name)
+    if name.startswith("window_gt_prefill"):
+        assert (g.labels == hk.LOCAL).all() and (g.count0 == w.P).all()
+    if name.startswith("uniform_ring_gt_prefill"):
+        A = w.N * w.rho[0] // w.rho[1]
+        assert A > w.P and (g.labels == hk.LOCAL).any() and (g.labels == hk.GLOBAL).any()
+        assert (g.cap[g.labels == hk.LOCAL] == A).all() and (g.count0 == w.P).all()
+
+
+SPLIT_CASES = {
+    "bf16_d128_short": small_config(head_dim=128, layers=2, rho=(1, 4), split_dist=20),
+    "bf16_d128_long": small_config(head_dim=128, heads=3, image_tokens=884, prefill_image=120,
+                                   split_dist=80, p_local=0.3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_CASES))
+def test_parity_split_calls(name):
+    """hkv_append + hkv_decode_attn + hkv_ste_evict as three calls per step,
+    replayed on the oracle (the standalone eviction stages its own queries)."""
+    w = SPLIT_CASES[name]
+    print(f"[gpu] parity split calls {name}: S={w.S} N={w.N} d={w.head_dim}", flush=True)
+    _check_all_groups(w, name, mode="split")
 
 
 def test_generator_twin_bits():
@@ -154,10 +199,22 @@ def test_generator_twin_bits():
             assert np.array_equal(bits_of(Q[sl]), qb)
 
 
-def test_fused_equals_separate_calls():
+FUSED_CASES = {
+    "bf16_d64": small_config(layers=2, batch=2, heads=8),
+    "f32_d64": small_config(dtype="f32", layers=2, heads=5),
+    "f32_d128": small_config(dtype="f32", head_dim=128, heads=4, rho=(1, 6), split_dist=40),
+    # bf16 d128: short-stream kernel (budget <= 192) and long-stream kernel
+    "bf16_d128_short": small_config(head_dim=128, layers=2, heads=6, split_dist=20),
+    "bf16_d128_long": small_config(head_dim=128, heads=3, image_tokens=884, prefill_image=120,
+                                   split_dist=80, p_local=0.3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_CASES))
+def test_fused_equals_separate_calls(name):
     """hkv_decode_step gives bit-identical results to append + attn + evict."""
-    w = small_config(layers=2, batch=2, heads=8)
-    print("[gpu] fused vs separate", flush=True)
+    w = FUSED_CASES[name]
+    print(f"[gpu] fused vs separate {name}", flush=True)
     inputs = device_inputs(w, 1)
     streams = list(range(w.S))
     a = gpu_generation(w, 1, streams, mode="fused", inputs=inputs)
@@ -185,13 +242,27 @@ def _events_of(w, seed=0):
     return O.run_group(w, K, V, Q), K, V
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
-def test_evict_given_identical_scores(dtype, d):
+EVICT_CASES = {
+    "bf16_d64": dict(),
+    "f32_d128": dict(dtype="f32", head_dim=128),
+    # bf16 d128 keys read from the state's scores: short-stream kernel (budget
+    # <= 192) and long-stream kernel (budget 221)
+    "bf16_d128_short": dict(head_dim=128),
+    "bf16_d128_long": dict(head_dim=128, image_tokens=884, prefill_image=120, split_dist=80),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EVICT_CASES))
+def test_evict_given_identical_scores(name):
     """Load the oracle's pre-eviction state (layout and fp32-rounded scores) into
     a GPU state and run hkv_ste_evict alone: the evicted set and the layout after
-    tail fill must equal the oracle's selection on the same fp32 scores, bit for bit."""
-    w = small_config(dtype=dtype, head_dim=d, heads=4, p_local=0.0, split_dist=20)
-    print(f"[gpu] evict given scores {dtype} d={d}", flush=True)
+    the eviction must equal the oracle's selection on the same fp32 scores, bit
+    for bit."""
+    kw = dict(heads=4, p_local=0.0, split_dist=20)
+    kw.update(EVICT_CASES[name])
+    w = small_config(**kw)
+    dtype = w.dtype
+    print(f"[gpu] evict given scores {name}", flush=True)
     rec, K, V = _events_of(w)
     events = rec.events[:12] + rec.events[-12:]
     assert events
@@ -230,7 +301,7 @@ def test_evict_given_identical_scores(dtype, d):
         got_pos = cache.pos[base:base + c].cpu().numpy().tolist()
         assert got_pos == want_pos
         got_sc = cache.score[base:base + c].cpu().numpy()
-        assert np.array_equal(got_sc, np.array(want_sc, dtype=np.float32))
+        assert np.array_equal(got_sc, sc32)              # the scores it ranked
         kept = [j for j in range(c) if j not in set(own)]
         got_k = cache.k_pool[base:base + c].float().cpu().numpy()[kept]
         want_k = torch.from_numpy(K[s][pos[kept]]).to(dt).float().numpy()

@@ -108,6 +108,29 @@ def _unstrat_highest(slot_pos, slot_score, t, w_obs, n_evict):         # keeps t
     order = lambda j: (-float(slot_score[j]), int(slot_pos[j]))
     return sorted(sorted(cand, key=order)[:n_evict])
 
+
+def _window_noncausal(Qwin, K, first_pos):           # every query sees the whole prefill
+    P = first_pos + Qwin.shape[0]
+    score = np.zeros(P)
+    for q in Qwin:
+        score += O.probs(q, K[:P])
+    return score
+
+
+def _window_last_only(Qwin, K, first_pos):           # only the newest query scores
+    P = first_pos + Qwin.shape[0]
+    return O.probs(Qwin[-1], K[:P])
+
+
+def _window_start_off_by_one(Qwin, K, first_pos):    # queries placed one position early
+    P = first_pos + Qwin.shape[0]
+    score = np.zeros(P)
+    for r, q in enumerate(Qwin):
+        i = first_pos + r - 1
+        score[: i + 1] += O.probs(q, K[: i + 1])
+    return score
+
+
 MUTANTS = {
     "label_le": ("label_of", _label_le),
     "count_forward": ("classify_count", _count_forward),
@@ -126,6 +149,9 @@ MUTANTS = {
                           lambda c, b, m, w: c == b + m - w + 2),
     "unstrat_no_protection": ("unstratified_select", _unstrat_no_protection),
     "unstrat_highest": ("unstratified_select", _unstrat_highest),
+    "window_noncausal": ("window_scores", _window_noncausal),
+    "window_last_only": ("window_scores", _window_last_only),
+    "window_start_off_by_one": ("window_scores", _window_start_off_by_one),
 }
 
 ALL_CHECKS = [
@@ -142,6 +168,7 @@ ALL_CHECKS = [
     lambda: pins.check_uniform_scores(O),
     lambda: pins.check_unstratified_bruteforce(O, trials=60),
     lambda: pins.check_variant_groups(O),
+    lambda: pins.check_window_scores(O),
 ]
 
 

@@ -224,10 +224,10 @@ def check_layout(orc, cfg, rec):
         assert set(final) == set(range(cfg.N)) - gone
 
 
-def run_small(orc, **kw):
+def run_small(orc, steps=None, **kw):
     cfg = small_config(**kw)
     K, V, Q = group_f64(cfg)
-    return cfg, orc.run_group(cfg, K, V, Q), K, Q
+    return cfg, orc.run_group(cfg, K, V, Q, steps=steps), K, Q
 
 
 def check_group_invariants(orc):
@@ -317,6 +317,90 @@ def check_uniform_scores(orc):
         far = sorted(pos[j] for j in cand if ev.t - pos[j] >= D)
         got = sorted(pos[j] for j in ev.evicted_slots)
         assert got == sorted(far[:4] + near[:4])
+
+
+# ---------------------------------------------------------------- initial-eviction scores
+def _fraction(x: str) -> Fraction:
+    return Fraction(x)
+
+
+def check_window_scores_uniform(orc):
+    """All window queries zero: query i gives each of positions 0..i the
+    probability 1/(i+1), so position j scores sum_{i=max(j, P-W)}^{P-1} 1/(i+1)
+    (a closed form that fixes causality, the window's first position and the
+    number of queries)."""
+    rng = np.random.default_rng(31)
+    for P, W, d in ((5, 3, 4), (12, 8, 64), (40, 8, 128), (9, 1, 8), (8, 8, 16)):
+        K = rng.normal(size=(P, d))
+        got = orc.window_scores(np.zeros((W, d)), K, P - W)
+        want = [sum(1.0 / (i + 1) for i in range(max(j, P - W), P)) for j in range(P)]
+        assert got.shape == (P,)
+        assert np.max(np.abs(got - np.array(want))) < 1e-12, (P, W)
+
+
+def _rational_window(ex):
+    """Keys (ln u_j, 0, 0, 0) and queries (2 a_r, 0, 0, 0) of a worked example."""
+    u = [int(x) for x in ex["u"].split()]
+    a = [int(x) for x in ex["a"].split()]
+    K = np.zeros((len(u), 4))
+    K[:, 0] = np.log(np.array(u, dtype=np.float64))
+    Q = np.zeros((len(a), 4))
+    Q[:, 0] = 2.0 * np.array(a, dtype=np.float64)
+    return K, Q
+
+
+def check_window_scores_golden(orc):
+    """Hand-worked initial-eviction scores with rational probabilities, and one
+    whole classification + initial eviction of a one-head group."""
+    for name, ex in read_sections("window_scores_worked.txt").items():
+        P, W = int(ex["P"]), int(ex["W"])
+        K, Q = _rational_window(ex)
+        got = orc.window_scores(Q, K, P - W)
+        want = [float(_fraction(x)) for x in ex["score"].split()]
+        assert np.max(np.abs(got - np.array(want))) < 1e-12, name
+        if "evicted_pos" not in ex:
+            continue
+        N = int(ex["N"])
+        num, den = (int(x) for x in ex["rho"].split("/"))
+        from hkv_inputs.configs import HkvConfig
+        cfg = HkvConfig(name=name, cid=99, layers=1, batch=1, heads=1, head_dim=4, dtype="f32",
+                        prefix=0, image_tokens=N, prefill_image=P,
+                        local_window=int(ex["window"]), rho=(num, den),
+                        split_dist=int(ex["split"]), w_obs=W, evict_m=W)
+        Kg = np.zeros((1, N, 4))
+        Kg[0, :P] = K
+        Qg = np.zeros((1, N - P + W, 4))
+        Qg[0, :W] = Q
+        rec = orc.run_group(cfg, Kg, np.zeros_like(Kg), Qg, steps=0)
+        assert rec.n_tokens == [int(ex["count"])], name
+        assert rec.labels == [orc.GLOBAL], name
+        assert rec.budget == (N * num) // den, name
+        assert len(rec.init_events) == 1, name
+        ev = rec.init_events[0]
+        assert sorted(ev.slot_pos[j] for j in ev.evicted_slots) == \
+            [int(x) for x in ex["evicted_pos"].split()], name
+        assert rec.tables_after_classify[0] == [int(x) for x in ex["table_after"].split()], name
+
+
+def check_init_score_sum(orc):
+    """Every initial eviction's scores sum to W: each of the W window queries
+    spreads probability 1 over positions that are all present at
+    classification."""
+    seen = 0
+    for kw in ({}, dict(rho=(1, 6), split_dist=20), dict(head_dim=128, rho=(1, 8), heads=4)):
+        cfg, rec, _, _ = run_small(orc, steps=0, **kw)
+        for ev in rec.init_events:
+            s = np.array(ev.slot_score)
+            assert abs(s.sum() - cfg.w_obs) < 1e-12
+            assert s.min() >= 0 and s.max() <= cfg.w_obs
+            seen += 1
+    assert seen > 0
+
+
+def check_window_scores(orc):
+    check_window_scores_uniform(orc)
+    check_window_scores_golden(orc)
+    check_init_score_sum(orc)
 
 
 # ---------------------------------------------------------------- ablation variants
@@ -445,3 +529,15 @@ def test_unstratified_bruteforce():
 
 def test_variant_groups():
     check_variant_groups(O)
+
+
+def test_window_scores_uniform():
+    check_window_scores_uniform(O)
+
+
+def test_window_scores_golden():
+    check_window_scores_golden(O)
+
+
+def test_init_score_sum():
+    check_init_score_sum(O)
