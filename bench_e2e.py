@@ -120,6 +120,36 @@ class Driver:
         # t-W+1 .. t is the contiguous run starting at slot (t + 1) mod W
         self.qring = [torch.zeros(self.per, 2 * W, d, dtype=model.dt, device=dev)
                       for _ in range(w.layers)]
+        self.rec = None     # optional recording of one (layer, sequence) group
+
+    def record(self, layer: int, seq: int, on_classified=None):
+        """One eager generation that keeps, for the streams of (layer, seq), the
+        rows handed to hkv_decode_step at every step (k, v, the newest query)
+        with its output and evicted positions, for a replay on another
+        implementation.  `on_classified()` runs between the classification and
+        the first step.  Returns the recording (device tensors)."""
+        import torch
+        w, dev = self.w, self.K.device
+        H, d, T, M = w.heads, w.head_dim, w.steps, w.evict_m
+        lo = seq * H                               # the group's rows inside the layer
+        rec = {"layer": layer, "rows": slice(lo, lo + H),
+               "k": torch.empty(T, H, d, dtype=self.m.dt, device=dev),
+               "v": torch.empty(T, H, d, dtype=self.m.dt, device=dev),
+               "q": torch.empty(T, H, d, dtype=self.m.dt, device=dev),
+               "out": torch.empty(T, H, d, dtype=self.m.dt, device=dev),
+               "log_all": torch.full((w.S, M), -1, dtype=torch.int32, device=dev),
+               "log": torch.empty(T, H, M, dtype=torch.int32, device=dev)}
+        self.rec = rec
+        try:
+            self._reset()
+            if on_classified is not None:
+                torch.cuda.synchronize()
+                on_classified()
+            self._loop(True)
+        finally:
+            self.rec = None
+        torch.cuda.synchronize()
+        return rec
 
     def _reset(self):
         """Eager: classification from the synthetic prefill, first token, query
@@ -162,8 +192,17 @@ class Driver:
                     vp = self.v.data_ptr() - s0 * d * eb
                     qw = self.qring[l].data_ptr() + ((t + 1) % W) * d * eb - s0 * 2 * W * d * eb
                     op = self.att.data_ptr() - s0 * d * eb
+                    rec = self.rec if (self.rec is not None and self.rec["layer"] == l) else None
                     hk.hkv_decode_step(self.cfg, st, t, kp, vp, d, qw, 2 * W * d, op, d,
-                                       None, s0, per, torch.cuda.current_stream())
+                                       None if rec is None else rec["log_all"], s0, per,
+                                       torch.cuda.current_stream())
+                    if rec is not None:
+                        r, i = rec["rows"], t - w.P
+                        rec["k"][i] = self.k.view(per, d)[r]
+                        rec["v"][i] = self.v.view(per, d)[r]
+                        rec["q"][i] = qv[r]
+                        rec["out"][i] = self.att.view(per, d)[r]
+                        rec["log"][i] = rec["log_all"][s0 + r.start:s0 + r.stop]
                 else:
                     self.att.copy_(self.v)
                 self.x.add_(self.att @ m.wo[l])

@@ -97,15 +97,9 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
         hk.hkv_classify(cfg, st, K, V, N * d, Q, w.q_rows * d)
     idx = torch.tensor(list(streams), dtype=torch.long, device=K.device)
     sl = list(streams)
-    lab = cache.label[idx].cpu().numpy()
-    cnt0 = cache.count[idx].cpu().numpy()
+    rec = state_after_classify(cache, sl)
     base0 = cache.base.cpu().numpy()
-    capv = cache.cap[idx].cpu().numpy()
-    rec = dict(streams=sl, labels=lab, n_tokens=cache.n_tokens[idx].cpu().numpy(),
-               budget=cache.budget[idx].cpu().numpy(), cap=capv,
-               count0=cnt0, tables0=_tables(cache, sl, cnt0),
-               scores0=[cache.score[int(base0[s]):int(base0[s]) + int(c)].cpu().numpy()
-                        for s, c in zip(sl, cnt0)])
+    capv = rec["cap"]
     T = w.steps if steps is None else steps
     trace = None
     if score_trace:
@@ -144,12 +138,8 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
     hk.hkv_check(cfg, st)
     if trace is not None:
         rec["score_trace"] = trace.cpu().numpy()
-    cntf = cache.count[idx].cpu().numpy()
     rec.update(outs=gen.decode(bits_of(outs), w.dtype), logs=logs.cpu().numpy(),
-               count_final=cntf, tables_final=_tables(cache, sl, cntf))
-    base = cache.base.cpu().numpy()
-    rec["scores_final"] = [cache.score[int(base[s]):int(base[s]) + int(c)].cpu().numpy()
-                           for s, c in zip(sl, cntf)]
+               **state_final(cache, sl))
     return GpuRecord(**rec)
 
 
@@ -198,15 +188,47 @@ def _evict_flag(slot_pos, slot_score, t, W, D, own: List[int], gpu: List[int]) -
     return True
 
 
+def state_after_classify(cache: hk.HkvCache, streams: Sequence[int]) -> dict:
+    """The recorded streams' classification results and initial layout."""
+    idx = torch.tensor(list(streams), dtype=torch.long, device=cache.label.device)
+    sl = list(streams)
+    cnt0 = cache.count[idx].cpu().numpy()
+    base0 = cache.base.cpu().numpy()
+    return dict(streams=sl, labels=cache.label[idx].cpu().numpy(),
+                n_tokens=cache.n_tokens[idx].cpu().numpy(),
+                budget=cache.budget[idx].cpu().numpy(), cap=cache.cap[idx].cpu().numpy(),
+                count0=cnt0, tables0=_tables(cache, sl, cnt0),
+                scores0=[cache.score[int(base0[s]):int(base0[s]) + int(c)].cpu().numpy()
+                         for s, c in zip(sl, cnt0)])
+
+
+def state_final(cache: hk.HkvCache, streams: Sequence[int]) -> dict:
+    """The recorded streams' layout and scores after the last step."""
+    idx = torch.tensor(list(streams), dtype=torch.long, device=cache.label.device)
+    sl = list(streams)
+    cntf = cache.count[idx].cpu().numpy()
+    base = cache.base.cpu().numpy()
+    return dict(count_final=cntf, tables_final=_tables(cache, sl, cntf),
+                scores_final=[cache.score[int(base[s]):int(base[s]) + int(c)].cpu().numpy()
+                              for s, c in zip(sl, cntf)])
+
+
 def oracle_check_group(w: HkvConfig, seed: int, l: int, b: int, g: GpuRecord,
-                       steps: Optional[int] = None, rep: Optional[Report] = None) -> Report:
+                       steps: Optional[int] = None, rep: Optional[Report] = None,
+                       arrays=None) -> Report:
+    """Replays group (l, b) on the oracle against the GPU record g.  `arrays`
+    (K, V, Q as float64 [H, N, d], [H, N, d], [H, N-P+W, d]) replaces the
+    seeded inputs, e.g. with the rows a model produced during decoding."""
     rep = rep or Report()
     H, P, W, D, N = w.heads, w.P, w.w_obs, w.split_dist, w.N
     if getattr(w, "unstratified", False):       # one subset holds every candidate
         D = 10 ** 9
     T = w.steps if steps is None else steps
-    kb, vb, qb = gen.group_inputs(w, seed, l, b)
-    K, Vv, Q = gen.decode(kb, w.dtype), gen.decode(vb, w.dtype), gen.decode(qb, w.dtype)
+    if arrays is None:
+        kb, vb, qb = gen.group_inputs(w, seed, l, b)
+        K, Vv, Q = gen.decode(kb, w.dtype), gen.decode(vb, w.dtype), gen.decode(qb, w.dtype)
+    else:
+        K, Vv, Q = arrays
     col = {s: i for i, s in enumerate(g.streams)}
     gi = [col[w.stream(l, b, h)] for h in range(H)]
 
