@@ -151,6 +151,23 @@ hkv_status hkv_classify(const hkv_config *cfg, hkv_state *st,
                         const void *k_stage, const void *v_stage, int64_t ld_stage,
                         const void *q_obs, int64_t ld_qobs, void *stream);
 
+/* hkv_classify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same classification and initial layout, bit for bit, with the classification
+ * scores kept in a buffer the library holds per device for the life of the
+ * process (32 MiB, taken when the library is first used on the device) instead
+ * of the state's workspace, which may be NULL here.  Nothing is allocated and
+ * no allocating routine is called.  The buffer needs S*P*4 bytes (S streams,
+ * P = prefill_len): larger configurations return HKV_E_UNSUPPORTED before
+ * anything is enqueued.  Every call on one device shares that buffer and keeps
+ * what the last call left in it, so calls that overlap on one device (on
+ * different streams, or from several threads without ordering) race; calls
+ * ordered on one stream do not.  Other arguments, outputs and errors are those
+ * of hkv_classify. */
+hkv_status hkv_classify_noalloc(const hkv_config *cfg, hkv_state *st,
+                                const void *k_stage, const void *v_stage, int64_t ld_stage,
+                                const void *q_obs, int64_t ld_qobs, void *stream);
+
 /* Steps 1-2 fused into the prefill attention (bf16): the causal attention of
  * every prefill position over the prefilled cache, written to `out` (stream s
  * row p at out + s*ld_out + p*head_dim), with the classification of

@@ -20,7 +20,8 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 __all__ = [
     "HkvError", "hkv_config", "hkv_state", "LOCAL", "GLOBAL", "FULL",
     "DT_BF16", "DT_F32", "make_config", "config_from_workload", "HkvCache",
-    "hkv_pool_slots", "hkv_workspace_bytes", "hkv_validate", "hkv_classify", "hkv_prefill",
+    "hkv_pool_slots", "hkv_workspace_bytes", "hkv_validate", "hkv_classify",
+    "hkv_classify_noalloc", "hkv_prefill",
     "hkv_append", "hkv_decode_attn", "hkv_ste_evict", "hkv_decode_step", "hkv_check",
     "hkv_status_string", "hkv_last_error", "LIB_PATH",
 ]
@@ -70,6 +71,8 @@ def _load():
         "hkv_validate": (c_int32, [cfgp]),
         "hkv_classify": (c_int32, [cfgp, stp, c_void_p, c_void_p, c_int64, c_void_p, c_int64,
                                    c_void_p]),
+        "hkv_classify_noalloc": (c_int32, [cfgp, stp, c_void_p, c_void_p, c_int64, c_void_p,
+                                           c_int64, c_void_p]),
         "hkv_prefill": (c_int32, [cfgp, stp, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                   c_void_p, c_int64, c_void_p]),
         "hkv_append": (c_int32, [cfgp, stp, c_int32, c_void_p, c_void_p, c_int64, c_int32,
@@ -170,6 +173,11 @@ def hkv_validate(cfg: hkv_config) -> int:
 
 def hkv_classify(cfg, state, k_stage, v_stage, ld_stage, q_obs, ld_qobs, stream=None):
     return _call("hkv_classify", ctypes.byref(cfg), ctypes.byref(state), _ptr(k_stage),
+                 _ptr(v_stage), ld_stage, _ptr(q_obs), ld_qobs, _stream(stream))
+
+
+def hkv_classify_noalloc(cfg, state, k_stage, v_stage, ld_stage, q_obs, ld_qobs, stream=None):
+    return _call("hkv_classify_noalloc", ctypes.byref(cfg), ctypes.byref(state), _ptr(k_stage),
                  _ptr(v_stage), ld_stage, _ptr(q_obs), ld_qobs, _stream(stream))
 
 

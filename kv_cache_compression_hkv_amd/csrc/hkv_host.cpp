@@ -90,7 +90,7 @@ hkv_status derive(const hkv_config* c, Derived* d) {
   return HKV_OK;
 }
 
-hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st) {
+hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st, bool need_workspace) {
   if (!st) return fail(HKV_E_INVAL, "state is NULL");
   if (!st->k_pool || !st->v_pool || !st->pos || !st->score || !st->base || !st->cap ||
       !st->count || !st->budget || !st->n_tokens || !st->label || !st->err ||
@@ -107,6 +107,7 @@ hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st) {
   Derived d;
   hkv_status s = derive(c, &d);
   if (s != HKV_OK) return s;
+  if (!need_workspace) return HKV_OK;
   if (!st->workspace || (reinterpret_cast<uintptr_t>(st->workspace) & 255u))
     return fail(HKV_E_INVAL, "workspace must be non-NULL and 256-byte aligned");
   if (st->workspace_bytes < d.ws_bytes)

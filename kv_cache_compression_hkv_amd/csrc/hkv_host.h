@@ -38,7 +38,10 @@ hkv_status fail(hkv_status st, const char* fmt, ...);
 void clear_error();
 const char* last_error();
 
-hkv_status check_state_buffers(const hkv_config* cfg, const hkv_state* st);
+// need_workspace = false skips the workspace checks (the entry point that keeps
+// its scratch in the library's own static buffer).
+hkv_status check_state_buffers(const hkv_config* cfg, const hkv_state* st,
+                               bool need_workspace = true);
 hkv_status check_range(const Derived& d, int32_t s_begin, int32_t s_count);
 hkv_status check_step(const hkv_config* cfg, int32_t t);
 hkv_status check_data_ptr(const void* p, int64_t ld, int elem_bytes, const char* what);

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "hkv_device.h"
 #include "hkv_host.h"
@@ -1746,6 +1747,13 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
 
 __global__ void k_reset_err(int* err) { *err = 0; }
 
+// Classification scores [S, P] of hkv_classify_noalloc: a file-scope buffer that
+// each device holds once for the life of the process, so that the call needs no
+// caller workspace and allocates nothing.  Host code never passes `scratch`
+// itself to a kernel: it uses the device address hipGetSymbolAddress returns.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
 }  // namespace dev
 
 // ------------------------------------------------------------------ host glue
@@ -1838,15 +1846,39 @@ extern "C" {
 
 // Classification (k_classify, or k_prefill when q_stage is given, which also
 // writes the prefill attention to `pout`) and initial layout (k_layout).
+// Device address of dev::scratch on the current device, looked up once per
+// device (each device holds its own copy of the buffer).
+static hkv_status noalloc_scratch(float** out) {
+  static std::mutex mu;
+  static float* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(HKV_E_UNSUPPORTED, "device index %d beyond 63", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(dev::scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HKV_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return HKV_OK;
+}
+
+// init_scores_override: where the classification scores go instead of the
+// state's workspace (NULL: the workspace).
 static hkv_status classify_impl(const hkv_config* c, hkv_state* st, const void* k_stage,
                                 const void* v_stage, int64_t ld_stage, const void* q_obs,
                                 int64_t ld_qobs, const void* q_stage, int64_t ld_q, void* pout,
-                                int64_t ld_out, void* stream) {
+                                int64_t ld_out, void* stream,
+                                float* init_scores_override = nullptr) {
   clear_error();
   Derived d;
   hkv_status r = derive(c, &d);
   if (r != HKV_OK) return r;
-  if ((r = check_state_buffers(c, st)) != HKV_OK) return r;
+  if ((r = check_state_buffers(c, st, init_scores_override == nullptr)) != HKV_OK) return r;
   const int eb = elem_bytes(c);
   if ((r = check_data_ptr(k_stage, ld_stage, eb, "k_stage")) != HKV_OK) return r;
   if ((r = check_data_ptr(v_stage, ld_stage, eb, "v_stage")) != HKV_OK) return r;
@@ -1869,8 +1901,10 @@ static hkv_status classify_impl(const hkv_config* c, hkv_state* st, const void* 
     if (c->w_obs > 8) return fail(HKV_E_UNSUPPORTED, "classification holds at most 8 queries");
   }
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(st->workspace);
-  float* init_scores = reinterpret_cast<float*>(ws + d.ws_init_scores);
+  float* init_scores = init_scores_override
+                           ? init_scores_override
+                           : reinterpret_cast<float*>(static_cast<char*>(st->workspace) +
+                                                      d.ws_init_scores);
 
   hipLaunchKernelGGL(dev::k_reset_err, dim3(1), dim3(1), 0, hs, st->err);
   if ((r = after_launch("reset")) != HKV_OK) return r;
@@ -1992,6 +2026,25 @@ hkv_status hkv_classify(const hkv_config* c, hkv_state* st, const void* k_stage,
                         int64_t ld_qobs, void* stream) {
   return classify_impl(c, st, k_stage, v_stage, ld_stage, q_obs, ld_qobs, nullptr, 0, nullptr, 0,
                        stream);
+}
+
+hkv_status hkv_classify_noalloc(const hkv_config* c, hkv_state* st, const void* k_stage,
+                                const void* v_stage, int64_t ld_stage, const void* q_obs,
+                                int64_t ld_qobs, void* stream) {
+  clear_error();
+  Derived d;
+  hkv_status r = derive(c, &d);
+  if (r != HKV_OK) return r;
+  const size_t need = size_t(d.S) * size_t(c->prefill_len) * sizeof(float);
+  if (need > dev::kNoAllocScratchBytes)
+    return fail(HKV_E_UNSUPPORTED,
+                "hkv_classify_noalloc: streams * prefill_len * 4 = %zu bytes exceeds its "
+                "%zu-byte scratch; use hkv_classify with a workspace",
+                need, dev::kNoAllocScratchBytes);
+  float* scr = nullptr;
+  if ((r = noalloc_scratch(&scr)) != HKV_OK) return r;
+  return classify_impl(c, st, k_stage, v_stage, ld_stage, q_obs, ld_qobs, nullptr, 0, nullptr, 0,
+                       stream, scr);
 }
 
 hkv_status hkv_prefill(const hkv_config* c, hkv_state* st, const void* q_stage, int64_t ld_q,
