@@ -33,7 +33,10 @@ import math
 import sys
 import time
 
-CHUNK = 16          # decode steps per captured graph
+# decode steps per captured graph: about 9e3 graph nodes at LlamaGen-XL's 36
+# layers.  A whole generation (about 3e5 nodes) in one graph ended the process
+# during instantiation, so graphs stay bounded by this.
+CHUNK = 16
 
 # generation-side width of each backbone: (MLP intermediate size, vocabulary)
 ARCH = {

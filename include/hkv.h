@@ -122,6 +122,11 @@ typedef struct {
   uint8_t *label;             /* [S] hkv_label (4-byte aligned)                */
   int32_t *free_slots;        /* [S, M] slots freed by the last eviction       */
   int32_t *n_free;            /* [S] of those, how many are still free         */
+  float   *qstat;             /* [S, w_obs, 4] per Global stream, the softmax
+                               * statistics of its last w_obs decode queries:
+                               * (max, 1/sum, step bits, 0), exp2 domain; written
+                               * by the attention, reset by classification,
+                               * 16-byte aligned                               */
   int32_t *err;               /* [1] sticky device error bits                  */
   void    *workspace;         /* hkv_workspace_bytes() bytes, 256-B aligned    */
   size_t   workspace_bytes;

@@ -49,6 +49,7 @@ class hkv_state(ctypes.Structure):
                 ("score", c_void_p), ("base", c_void_p), ("cap", c_void_p),
                 ("count", c_void_p), ("budget", c_void_p), ("n_tokens", c_void_p),
                 ("label", c_void_p), ("free_slots", c_void_p), ("n_free", c_void_p),
+                ("qstat", c_void_p),
                 ("err", c_void_p), ("workspace", c_void_p), ("workspace_bytes", c_size_t),
                 ("phase", c_int32)]
 
@@ -239,6 +240,7 @@ class HkvCache:
         self.label = torch.zeros((S,), dtype=torch.uint8, device=dev)
         self.free_slots = torch.zeros((S, max(1, cfg.evict_m)), dtype=torch.int32, device=dev)
         self.n_free = torch.zeros((S,), dtype=torch.int32, device=dev)
+        self.qstat = torch.zeros((S, max(1, cfg.w_obs), 4), dtype=torch.float32, device=dev)
         self.err = torch.zeros((1,), dtype=torch.int32, device=dev)
         nbytes = hkv_workspace_bytes(cfg)
         self.workspace = torch.zeros((nbytes + 256,), dtype=torch.uint8, device=dev)
@@ -249,4 +251,5 @@ class HkvCache:
             self.score.data_ptr(), self.base.data_ptr(), self.cap.data_ptr(),
             self.count.data_ptr(), self.budget.data_ptr(), self.n_tokens.data_ptr(),
             self.label.data_ptr(), self.free_slots.data_ptr(), self.n_free.data_ptr(),
+            self.qstat.data_ptr(),
             self.err.data_ptr(), ws_aligned, nbytes, 0)

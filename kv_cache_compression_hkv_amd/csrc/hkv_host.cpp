@@ -94,10 +94,10 @@ hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st, bool ne
   if (!st) return fail(HKV_E_INVAL, "state is NULL");
   if (!st->k_pool || !st->v_pool || !st->pos || !st->score || !st->base || !st->cap ||
       !st->count || !st->budget || !st->n_tokens || !st->label || !st->err ||
-      !st->free_slots || !st->n_free)
+      !st->free_slots || !st->n_free || !st->qstat)
     return fail(HKV_E_INVAL, "state has a NULL buffer");
-  if (!aligned16(st->k_pool) || !aligned16(st->v_pool))
-    return fail(HKV_E_INVAL, "k_pool/v_pool must be 16-byte aligned");
+  if (!aligned16(st->k_pool) || !aligned16(st->v_pool) || !aligned16(st->qstat))
+    return fail(HKV_E_INVAL, "k_pool, v_pool and qstat must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(st->base) & 7u) || (reinterpret_cast<uintptr_t>(st->pos) & 3u) ||
       (reinterpret_cast<uintptr_t>(st->score) & 3u) || (reinterpret_cast<uintptr_t>(st->label) & 3u) ||
       (reinterpret_cast<uintptr_t>(st->count) & 3u) || (reinterpret_cast<uintptr_t>(st->cap) & 3u) ||

@@ -75,6 +75,17 @@ constexpr int kNT = kNW * kWave;
 #ifndef HKV_UE_L
 #define HKV_UE_L 2
 #endif
+// ... when that pass is the only one (window statistics from the ring)
+#ifndef HKV_UER_S
+#define HKV_UER_S 1
+#endif
+#ifndef HKV_UER_L
+#define HKV_UER_L 2
+#endif
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2):
 // block b runs on XCD b % 8.  Mapping each XCD to a contiguous run of streams
 // keeps the streams that share a cache line of per-stream data (16 per 64 B)
@@ -105,6 +116,7 @@ struct StepArgs {
   const long long* base; int* count; const int* budget; const int* cap;
   const unsigned char* label;
   int* free_slots; int* n_free;
+  float4* qstat;                       // [S, W] ring of query statistics (max, 1/sum, step)
   int* err;
   float* ws_tile; int* ws_pos; uint64_t* ws_keys;   // per-slot spill
   int s_begin, t, w, W, M, D;
@@ -247,6 +259,7 @@ struct StepCfg {
   static constexpr int kRows =
       !kB16 ? HKV_U_F32 : (D == 64 ? HKV_U_B64 : (C ? HKV_U_B128L : HKV_U_B128S));
   static constexpr int kTilesInFlight = C ? HKV_UE_L : HKV_UE_S;
+  static constexpr int kTilesInFlightRing = C ? HKV_UER_L : HKV_UER_S;
   static constexpr bool kKeys = kB16 && !StepMfmaAttn<T, D>::value;
   static constexpr int kOnePass = kKeys && !C ? HKV_ONEPASS_S : 0;
   static constexpr int kSlots =
@@ -262,12 +275,21 @@ struct QStage {
   static constexpr int kPitch = D / 4 + 2;   // row pitch in 8-byte units
 };
 
+// Window statistics of an eviction taken from the query-statistics ring when
+// its entries are current (1), or always formed by the eviction itself (0).
+#ifndef HKV_RING
+#define HKV_RING 1
+#endif
+
 template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
                                             EvictShared& es, uint64_t* skeys, bool tile_ready,
-                                            uint2* qs, bool q_staged) {
+                                            uint2* qs, bool q_staged, bool cur_known,
+                                            float cur_m, float cur_il) {
   // (returns the number of freed slots: M, or 0 if nothing was evicted; skeys:
-  // on-chip room for kNT keys, free once the eviction starts)
+  // on-chip room for kNT keys, free once the eviction starts; es.cnt zeroed
+  // by the caller before a barrier; cur_known: this launch's attention gave
+  // the current query's softmax max cur_m and 1/sum cur_il)
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -276,7 +298,6 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
   const int s = x.s, c = x.c, slot_new = x.slot_new;
   const int t = a.t, W = a.W, Dd = a.D;
 
-  if (tid < 2) es.cnt[tid] = 0;
   const bool window = a.q_win != nullptr;
   constexpr uint64_t kNone = ~0ull;    // no slot (subset field 3)
   // slots tid + k*kNT, k < SPT, have their keys in registers for the selection;
@@ -300,7 +321,30 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
     // second writing the keys directly to the scratch.  Without one the keys
     // come from the state's scores.
     int nn = 0, nf = 0;                // subset sizes seen by this wave
-    const bool one_pass = window && c <= OC::kOnePass;
+    // statistics of the W window queries from the ring: the attention of each
+    // of the last W decode steps left its query's max and 1/sum there (the
+    // current one's also come from this launch's attention).  No eviction
+    // happens inside the window (M = W), so the slots a window query saw are
+    // exactly those whose position does not exceed its own, and its
+    // probabilities follow from its logits and these two numbers.  Lane i < W
+    // holds query i's; a stale entry (a step whose attention did not run)
+    // sends the stream down the path that forms the statistics itself.
+    float rm = 0.f, ril = 0.f;
+    bool rok = true;
+    if (window && lane < W) {
+      const int step = t - W + 1 + lane;
+      if (lane == W - 1 && cur_known) {
+        rm = cur_m;
+        ril = cur_il;
+      } else {
+        const float4 e = a.qstat[(long long)s * W + step % W];
+        rm = e.x;
+        ril = e.y;
+        rok = __float_as_int(e.z) == step;
+      }
+    }
+    const bool ring = HKV_RING && window && __ballot(!rok) == 0;   // (the same in every wave)
+    const bool one_pass = window && !ring && c <= OC::kOnePass;
     keys_in_scratch = !one_pass;
     if (window) {
       // v_mfma_f32_16x16x32_bf16: A = the W queries (rows W..15 zero), B = 16
@@ -331,8 +375,8 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       const int ntile = (c + 15) / 16;
       // one pass over the slots' key tiles: UE tiles in flight per wave (absent
       // tiles skipped, ragged columns zeroed); body(j, valid, position, logits)
-      auto tiles = [&](auto&& body) {
-        constexpr int UE = OC::kTilesInFlight;
+      auto tiles = [&](auto ue, auto&& body) {
+        constexpr int UE = decltype(ue)::value;
         for (int kt0 = wave; kt0 < ntile; kt0 += kNW * UE) {
           uint4 kb[UE][KC];
           int pj[UE];
@@ -368,16 +412,18 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         }
       };
 
-      // pass 1: each lane's online softmax statistics of its 4 query rows over
-      // the slots each query sees; reduced over the 16 key columns, then waves
-      // (one pass: also the tile and the positions)
+      // pass 1 (without the ring's statistics): each lane's online softmax
+      // statistics of its 4 query rows over the slots each query sees; reduced
+      // over the 16 key columns, then waves (one pass: also the tile and the
+      // positions)
+      if (!ring) {
       float wm[4], wl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         wm[r] = kNeg;
         wl[r] = 0.f;
       }
-      tiles([&](int j, bool vj, int pj, const f32x4& acc) {
+      tiles(Int<OC::kTilesInFlight>{}, [&](int j, bool vj, int pj, const f32x4& acc) {
         if (one_pass && lk == 0 && vj) sc.pos[j] = pj;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -417,6 +463,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         es.ql[tid] = 1.0f / L;
       }
       __syncthreads();                 // window statistics (and tile) complete
+      }
 
       if (one_pass) {
         // scores from the tile: thread tid owns slots tid + k*kNT
@@ -441,19 +488,21 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         // pass 2: the same logits, now as probabilities summed over each slot's
         // visible queries (rows 0-3 in lanes 0-15, rows 4-7 in lanes 16-31);
         // lanes 0-15 write the keys
-        float qm_r[4], ql_r[4];
+        // (probability = 2^(logit - max) / sum = 2^(logit - (max + log2 sum)))
+        float qm_r[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = lk * 4 + r;
-          qm_r[r] = i < W ? es.qm[i] : 0.f;
-          ql_r[r] = i < W ? es.ql[i] : 0.f;
+          const float m_ring = __shfl(rm, i & 15), il_ring = __shfl(ril, i & 15);
+          const float m = ring ? m_ring : es.qm[i & 7], il = ring ? il_ring : es.ql[i & 7];
+          qm_r[r] = i < W ? m - __log2f(il) : 0.f;
         }
-        tiles([&](int j, bool vj, int pj, const f32x4& acc) {
+        auto key_of = [&](int j, bool vj, int pj, const f32x4& acc) {
           float pr = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = lk * 4 + r;
-            if (vj && i < W && pj <= t - W + 1 + i) pr += exp2f(acc[r] * a.scale_log2 - qm_r[r]) * ql_r[r];
+            if (vj && i < W && pj <= t - W + 1 + i) pr += exp2f(acc[r] * a.scale_log2 - qm_r[r]);
           }
           pr += __shfl_xor(pr, 16);
           const bool own = lk == 0 && vj;
@@ -461,7 +510,13 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
           if (own) sc.keys[j] = make_skey(sb, pr, pj);
           nn += __popcll(__ballot(own && sb == 0));
           nf += __popcll(__ballot(own && sb == 1));
-        });
+        };
+        // with the ring's statistics this is the only pass over K: more of its
+        // tiles in flight
+        if (ring)
+          tiles(Int<OC::kTilesInFlightRing>{}, key_of);
+        else
+          tiles(Int<OC::kTilesInFlight>{}, key_of);
       }
     } else {
       __syncthreads();                 // subset counters zeroed before any wave adds
@@ -1189,35 +1244,44 @@ void k_step(StepArgs a) {
       }
     }
   }
+  if (EV && due && tid < 2) es.cnt[tid] = 0;   // subset sizes (before a barrier)
+  float cur_m = 0.f, cur_il = 0.f;              // current query: softmax max, 1/sum
   if (AT || tile_here) {
     // combine the waves
     __syncthreads();
+    float Mx = cs.m[0];
+#pragma unroll
+    for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) {
+      const float fw = exp2f(cs.m[w2] - Mx);
+      L = fmaf(cs.l[w2], fw, L);
+      if (AT && tid < D) o = fmaf(cs.o[w2][tid], fw, o);
+    }
+    cur_m = Mx;
+    cur_il = 1.0f / L;
     if (tile_here && tid < a.W) {        // statistics of window query tid
-      const bool cur = tid == a.W - 1;
-      float Mq = kNeg;
+      float Mq = Mx, Iq = cur_il;
+      if (tid != a.W - 1) {
+        Mq = kNeg;
 #pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2) Mq = fmaxf(Mq, cur ? cs.m[w2] : cs.wm[w2][tid]);
-      float Lq = 0.f;
+        for (int w2 = 0; w2 < kNW; ++w2) Mq = fmaxf(Mq, cs.wm[w2][tid]);
+        float Lq = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2)
-        Lq += (cur ? cs.l[w2] : cs.wl[w2][tid]) * exp2f((cur ? cs.m[w2] : cs.wm[w2][tid]) - Mq);
+        for (int w2 = 0; w2 < kNW; ++w2) Lq += cs.wl[w2][tid] * exp2f(cs.wm[w2][tid] - Mq);
+        Iq = 1.0f / Lq;
+      }
       es.qm[tid] = Mq;
-      es.ql[tid] = 1.0f / Lq;
+      es.ql[tid] = Iq;
     }
     if (AT && tid < D) {
-      float Mx = cs.m[0];
-#pragma unroll
-      for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
-      float L = 0.f, o = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kNW; ++w2) {
-        const float fw = exp2f(cs.m[w2] - Mx);
-        L = fmaf(cs.l[w2], fw, L);
-        o = fmaf(cs.o[w2][tid], fw, o);
-      }
       T* op = reinterpret_cast<T*>(a.out + ((long long)s * a.ld_o) * ES);
       op[tid] = F::from_f32(o / L);
     }
+    // the ring entry of this step: what a later eviction scores this query with
+    if (AT && glob && tid == 0)
+      a.qstat[(long long)s * a.W + a.t % a.W] = make_float4(Mx, cur_il, __int_as_float(a.t), 0.f);
   }
 
   // ---------------- Stratified Token Eviction (due Global streams)
@@ -1230,9 +1294,11 @@ void k_step(StepArgs a) {
       static_assert(sizeof(cs.o) >= kNT * sizeof(uint64_t), "combine buffer holds kNT keys");
       uint64_t* skeys = reinterpret_cast<uint64_t*>(&cs.o[0][0]);
       if (onchip)
-        nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, skeys, ready, lds_qw, q_staged);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, skeys, ready, lds_qw, q_staged, AT,
+                                             cur_m, cur_il);
       else
-        nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, skeys, ready, lds_qw, q_staged);
+        nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, skeys, ready, lds_qw, q_staged, AT,
+                                             cur_m, cur_il);
     } else if (a.log && tid < a.M) {
       a.log[(long long)s * a.M + tid] = -1;
     }
@@ -1254,6 +1320,11 @@ struct ClassifyArgs {
   float tau, scale_log2;
 };
 
+// bf16 classification logits on the matrix cores (1) or the vector ALUs (0).
+#ifndef HKV_CLASSIFY_MFMA
+#define HKV_CLASSIFY_MFMA 1
+#endif
+
 template <class T, int D>
 __global__ __launch_bounds__(kNT) void k_classify(ClassifyArgs a) {
   using F = Frag<T>;
@@ -1263,44 +1334,93 @@ __global__ __launch_bounds__(kNT) void k_classify(ClassifyArgs a) {
   __shared__ float mrow[WM], lrow[WM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.x;
+  const int s = xcd_block(blockIdx.x, gridDim.x);
   const int P = a.P, W = a.W;
-  const int g = lane / G, sub = lane % G;
 
-  float qv[WM][VE];
+  if constexpr (sizeof(T) == 2 && HKV_CLASSIFY_MFMA) {
+    // bf16: the W x P logit tile on the matrix cores, v_mfma_f32_16x16x32_bf16
+    // with A = the W queries (rows W..15 zero) and B = 16 keys per tile; lane l
+    // holds A row l%16 and B column (key) l%16 at head elements (l/16)*8 + 32*kc
+    // .. +7 and receives D rows (queries) (l/16)*4 .. +3 of key column l%16.
+    // Each wave takes every fourth 16-key tile, UT tiles of loads in flight.
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int KC = D / 32;
+    constexpr int UT = D == 64 ? 4 : 3;
+    const int li = lane & 15, lk = lane >> 4;
+    bf16x8 qa[KC];
 #pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    float qf[VE];
-    if (i < W) {
-      F::to_f32(ld16(a.q_obs + ((long long)s * a.ld_qobs + (long long)i * D + sub * VE) * ES), qf);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VE; ++e) qf[e] = 0.f;
+    for (int kc = 0; kc < KC; ++kc) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (li < W) u = ld16_once(a.q_obs + ((long long)s * a.ld_qobs + (long long)li * D + lk * 8 + kc * 32) * ES);
+      qa[kc] = __builtin_bit_cast(bf16x8, u);
     }
+    const char* kbase = a.k_stage + ((long long)s * a.ld_stage + lk * 8) * ES;
+    const int ntile = (P + 15) / 16;
+    for (int t0 = wave; t0 < ntile; t0 += kNW * UT) {
+      uint4 kb[UT][KC];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) qv[i][e] = qf[e] * a.scale_log2;
-  }
-
-  const char* kb = a.k_stage + ((long long)s * a.ld_stage + sub * VE) * ES;
-  for (int j0 = wave * R; j0 < P; j0 += kNW * R) {
-    const int j = j0 + g;
-    float kf[VE];
-    if (j < P) {
-      F::to_f32(ld16(kb + (long long)j * D * ES), kf);
-    } else {
+      for (int u = 0; u < UT; ++u) {
+        const int j = min((t0 + u * kNW) * 16 + li, P - 1);    // ragged tail: clamp
 #pragma unroll
-      for (int e = 0; e < VE; ++e) kf[e] = 0.f;
+        for (int kc = 0; kc < KC; ++kc)
+          kb[u][kc] = (t0 + u * kNW < ntile) ? ld16_stream(kbase + ((long long)j * D + kc * 32) * ES)
+                                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        if (t0 + u * kNW >= ntile) break;                     // uniform
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kc], __builtin_bit_cast(bf16x8, kb[u][kc]),
+                                                        acc, 0, 0, 0);
+        const int j = (t0 + u * kNW) * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = lk * 4 + r;
+          if (i < W && j < P) lg[i * P + j] = acc[r] * a.scale_log2;
+        }
+      }
     }
-    float mine = 0.f;
+  } else {
+    // vector ALU, G lanes per key row, every observation query in registers
+    const int g = lane / G, sub = lane % G;
+    float qv[WM][VE];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      float d0 = 0.f;
+      float qf[VE];
+      if (i < W) {
+        F::to_f32(ld16(a.q_obs + ((long long)s * a.ld_qobs + (long long)i * D + sub * VE) * ES), qf);
+      } else {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) d0 = fmaf(qv[i][e], kf[e], d0);
-      d0 = group_sum<G>(d0);
-      if (i == sub) mine = d0;
+        for (int e = 0; e < VE; ++e) qf[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) qv[i][e] = qf[e] * a.scale_log2;
     }
-    if (j < P && sub < W) lg[sub * P + j] = mine;
+
+    const char* kb = a.k_stage + ((long long)s * a.ld_stage + sub * VE) * ES;
+    for (int j0 = wave * R; j0 < P; j0 += kNW * R) {
+      const int j = j0 + g;
+      float kf[VE];
+      if (j < P) {
+        F::to_f32(ld16(kb + (long long)j * D * ES), kf);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) kf[e] = 0.f;
+      }
+      float mine = 0.f;
+#pragma unroll
+      for (int i = 0; i < WM; ++i) {
+        float d0 = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) d0 = fmaf(qv[i][e], kf[e], d0);
+        d0 = group_sum<G>(d0);
+        if (i == sub) mine = d0;
+      }
+      if (j < P && sub < W) lg[sub * P + j] = mine;
+    }
   }
   __syncthreads();
 
@@ -1629,6 +1749,7 @@ struct LayoutArgs {
   int* pos; float* score;
   long long* base; int* cap; int* count; int* budget; int* n_tokens; unsigned char* label;
   int* n_free;
+  float4* qstat;
   int* err;
   int H, N, P, w, W, M, D, A, full, uniform;
   long long group_slots;
@@ -1688,6 +1809,8 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
     a.count[s] = s_count;
     a.n_free[s] = 0;
   }
+  // no decode query yet: every ring entry stale
+  if (tid < a.W) a.qstat[(long long)s * a.W + tid] = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
   __syncthreads();
   const long long base = s_base;
   const int mode = s_mode;
@@ -1812,6 +1935,7 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.label = st->label;
   a.free_slots = st->free_slots;
   a.n_free = st->n_free;
+  a.qstat = reinterpret_cast<float4*>(st->qstat);
   a.err = st->err;
   a.ws_tile = reinterpret_cast<float*>(ws + d.ws_tile);
   a.ws_pos = reinterpret_cast<int*>(ws + d.ws_pos);
@@ -1992,6 +2116,7 @@ static hkv_status classify_impl(const hkv_config* c, hkv_state* st, const void* 
   b.n_tokens = st->n_tokens;
   b.label = st->label;
   b.n_free = st->n_free;
+  b.qstat = reinterpret_cast<float4*>(st->qstat);
   b.err = st->err;
   b.H = c->heads;
   b.N = c->final_len;

@@ -49,7 +49,7 @@ hkv_state fake_state(const hkv_config& c, int phase) {
   st.k_pool = st.v_pool = a;
   st.pos = st.count = st.cap = st.budget = st.n_tokens = st.free_slots = st.n_free = st.err =
       static_cast<int32_t*>(a);
-  st.score = static_cast<float*>(a);
+  st.score = st.qstat = static_cast<float*>(a);
   st.base = static_cast<int64_t*>(a);
   st.label = static_cast<uint8_t*>(a);
   st.workspace = a;

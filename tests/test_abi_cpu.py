@@ -80,7 +80,8 @@ def _fake_state(cfg, phase=1):
     """A state whose pointers are aligned but never dereferenced: every call
     below fails its host checks before anything is enqueued."""
     a = 1 << 20
-    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg), phase)
+    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg),
+                      phase)
     return st
 
 
@@ -116,7 +117,7 @@ def test_entry_points_reject_before_launch():
         with pytest.raises(hk.HkvError) as e:
             fn()
         assert e.value.status == code, (i, hk.hkv_last_error())
-    bad = hk.hkv_state(*([0] * 14), 0, 1)
+    bad = hk.hkv_state(*([0] * 15), 0, 1)
     with pytest.raises(hk.HkvError) as e:
         hk.hkv_append(cfg, bad, 40, buf, buf, 64, 0, 16)
     assert e.value.status == hk.E_INVAL

@@ -199,6 +199,18 @@ def test_generator_twin_bits():
             assert np.array_equal(bits_of(Q[sl]), qb)
 
 
+@pytest.mark.parametrize("name", sorted(SPLIT_CASES))
+def test_parity_stale_query_statistics(name):
+    """Separate calls with the attention left out on every fifth step: an
+    eviction whose window holds such a step finds stale entries in the state's
+    query-statistics ring and forms the window's statistics itself.  Its
+    decisions, and the outputs of the steps that attended, still match the
+    oracle."""
+    w = SPLIT_CASES[name]
+    print(f"[gpu] parity, attention skipped every fifth step {name}", flush=True)
+    _check_all_groups(w, name, mode="split", skip_attn=lambda t: t % 5 == 3)
+
+
 FUSED_CASES = {
     "bf16_d64": small_config(layers=2, batch=2, heads=8),
     "f32_d64": small_config(dtype="f32", layers=2, heads=5),

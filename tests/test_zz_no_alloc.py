@@ -16,11 +16,14 @@ from hkv_inputs.gpu import device_inputs
 from tests._fixtures import small_config
 
 FIELDS = ("k_pool", "v_pool", "pos", "score", "base", "cap", "count", "budget", "n_tokens",
-          "label", "free_slots", "n_free", "err")
+          "label", "free_slots", "n_free", "qstat", "err")
 
 
 def _bits(t):
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+    # bit patterns, so that equal NaN tags compare equal
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
 
 
 def _compare(w, seed):
@@ -60,7 +63,7 @@ def test_noalloc_rejects_oversized():
     cfg = hk.config_from_workload(w)
     assert w.S * w.P * 4 > 32 << 20
     a = 1 << 20
-    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, None, 0, 0)
+    st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, a, None, 0, 0)
     with pytest.raises(hk.HkvError) as e:
         hk.hkv_classify_noalloc(cfg, st, a, a, w.N * w.head_dim, a, w.q_rows * w.head_dim)
     assert e.value.status == hk.E_UNSUPPORTED
