@@ -177,21 +177,37 @@ class Generation:
             events[1].record(stream)
 
 
-def decode_per_layer(gen_obj, stream):
+# decode steps per captured graph of the per-layer loop: a graph of a whole
+# generation holds up to 1.4e5 launches (Lumina-mGPT, split step), and the HIP
+# runtime ended the process on the host while instantiating one of that size
+GRAPH_STEPS = 64
+
+
+def decode_per_layer(gen_obj, stream, n_split=0, t_begin=None, t_end=None):
     """The decode loop as a model runs it: at every step one launch per layer,
-    each over that layer's batch x heads streams."""
+    each over that layer's batch x heads streams (n_split > 0: the split decode
+    step, two kernels per layer).  Steps t_begin .. t_end-1 (default all)."""
     w, hk, st = gen_obj.w, gen_obj.hk, gen_obj.cache.state
     d, per = w.head_dim, w.batch * w.heads
-    for t in range(w.P, w.N):
+    t_begin = w.P if t_begin is None else t_begin
+    t_end = w.N if t_end is None else t_end
+    for t in range(t_begin, t_end):
         for l in range(w.layers):
-            hk.hkv_decode_step(gen_obj.cfg, st, t, gen_obj.kp[t], gen_obj.vp[t], w.N * d,
-                               gen_obj.qw[t], w.q_rows * d, gen_obj.out, d, None, l * per, per,
-                               stream)
+            if n_split:
+                hk.hkv_decode_step_split(gen_obj.cfg, st, t, gen_obj.kp[t], gen_obj.vp[t],
+                                         w.N * d, gen_obj.qw[t], w.q_rows * d, gen_obj.out, d,
+                                         None, l * per, per, n_split, stream)
+            else:
+                hk.hkv_decode_step(gen_obj.cfg, st, t, gen_obj.kp[t], gen_obj.vp[t], w.N * d,
+                                   gen_obj.qw[t], w.q_rows * d, gen_obj.out, d, None, l * per,
+                                   per, stream)
 
 
-def time_per_layer(gen_obj, steps):
-    """Per-layer decode loop, launched eagerly and replayed as one HIP graph
-    (captured once; every replay follows an eager classification)."""
+def time_per_layer(gen_obj, steps, splits=(2, 4, 8)):
+    """Per-layer decode loop, launched eagerly and replayed as HIP graphs of
+    GRAPH_STEPS steps each (captured once; every replay follows an eager
+    classification); then the split decode step replayed the same way for each
+    n_split in `splits`."""
     import numpy as np
     import torch
     w, hk = gen_obj.w, gen_obj.hk
@@ -216,26 +232,44 @@ def time_per_layer(gen_obj, steps):
         hk.hkv_check(gen_obj.cfg, gen_obj.cache.state)
         return float(np.mean(out))
 
+    def graphed(n_split):
+        classify()
+        torch.cuda.synchronize()
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(cur)
+        t0 = time.perf_counter()
+        for tb in range(w.P, w.N, GRAPH_STEPS):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                graph.capture_begin()
+                decode_per_layer(gen_obj, side, n_split, tb, min(w.N, tb + GRAPH_STEPS))
+                graph.capture_end()
+            graphs.append(graph)
+        torch.cuda.synchronize()
+        capture_s = time.perf_counter() - t0
+
+        def replay():
+            for g in graphs:
+                g.replay()
+        ms = timed(replay)
+        del graphs
+        return ms, capture_s
+
     eager = timed(lambda: decode_per_layer(gen_obj, cur))
-    classify()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(cur)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(side):
-        graph.capture_begin()
-        decode_per_layer(gen_obj, side)
-        graph.capture_end()
-    torch.cuda.synchronize()
-    capture_s = time.perf_counter() - t0
-    replay = timed(graph.replay)
-    launches = w.steps * w.layers
-    return {"launches_per_step": w.layers, "streams_per_launch": w.batch * w.heads,
-            "eager_ms_per_gen": round(eager, 3), "graph_ms_per_gen": round(replay, 3),
-            "graph_tokens_per_s": round(w.batch * w.steps / (replay * 1e-3), 1),
-            "graph_us_per_launch": round(replay * 1e3 / launches, 3),
-            "capture_s": round(capture_s, 2)}
+    replay, capture_s = graphed(0)
+    layer_steps = w.steps * w.layers
+    res = {"launches_per_step": w.layers, "streams_per_launch": w.batch * w.heads,
+           "eager_ms_per_gen": round(eager, 3), "graph_ms_per_gen": round(replay, 3),
+           "graph_tokens_per_s": round(w.batch * w.steps / (replay * 1e-3), 1),
+           "graph_us_per_launch": round(replay * 1e3 / layer_steps, 3),
+           "capture_s": round(capture_s, 2), "split": {}}
+    for n in splits:
+        ms, _ = graphed(n)
+        res["split"][str(n)] = {"graph_ms_per_gen": round(ms, 3),
+                                "graph_us_per_layer_step": round(ms * 1e3 / layer_steps, 3),
+                                "graph_tokens_per_s": round(w.batch * w.steps / (ms * 1e-3), 1)}
+    return res
 
 
 def time_prefill(w, inputs, hk, full_cache_of, reps: int = 5) -> dict:

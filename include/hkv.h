@@ -257,6 +257,25 @@ hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
                            int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
                            void *stream);
 
+/* hkv_decode_step for launches with few streams, such as one layer of a model
+ * (a few hundred to a thousand streams give a few workgroups per compute unit,
+ * and each launch then lasts as long as its slowest stream).  Pages: section
+ * "Methodology", step 3, as for hkv_decode_step, and the end-to-end speedups of
+ * section "Results", which a model measures layer by layer.  Each stream's
+ * table rows are spread over n_split workgroups (1 .. 8) that each leave a
+ * partial softmax state in the state's workspace; a second kernel on `stream`
+ * merges them into the output, writes the stream metadata back and runs the
+ * eviction of due Global streams.  Arguments, layouts, outputs and errors are
+ * those of hkv_decode_step, and so are the results except for the order of
+ * floating-point sums (outputs agree to rounding; a decision changes only where
+ * two scores lie that close).  Calls on one state must not overlap: the
+ * partial states live in its workspace.  n_split outside [1, 8]: HKV_E_INVAL. */
+hkv_status hkv_decode_step_split(const hkv_config *cfg, hkv_state *st, int32_t t,
+                                 const void *k_new, const void *v_new, int64_t ld_kv,
+                                 const void *q_win, int64_t ld_qw, void *out, int64_t ld_o,
+                                 int32_t *evicted_pos_log, int32_t s_begin, int32_t s_count,
+                                 int32_t n_split, void *stream);
+
 /* Synchronises `stream`, reads *err and maps it: CAPACITY bit -> HKV_E_CAPACITY,
  * other bits -> HKV_E_STATE, 0 -> HKV_OK.  Does not clear the word. */
 hkv_status hkv_check(const hkv_config *cfg, const hkv_state *st, void *stream);

@@ -22,7 +22,8 @@ __all__ = [
     "DT_BF16", "DT_F32", "make_config", "config_from_workload", "HkvCache",
     "hkv_pool_slots", "hkv_workspace_bytes", "hkv_validate", "hkv_classify",
     "hkv_classify_noalloc", "hkv_prefill",
-    "hkv_append", "hkv_decode_attn", "hkv_ste_evict", "hkv_decode_step", "hkv_check",
+    "hkv_append", "hkv_decode_attn", "hkv_ste_evict", "hkv_decode_step",
+    "hkv_decode_step_split", "hkv_check",
     "hkv_status_string", "hkv_last_error", "LIB_PATH",
 ]
 
@@ -85,6 +86,9 @@ def _load():
         "hkv_decode_step": (c_int32, [cfgp, stp, c_int32, c_void_p, c_void_p, c_int64, c_void_p,
                                       c_int64, c_void_p, c_int64, c_void_p, c_int32, c_int32,
                                       c_void_p]),
+        "hkv_decode_step_split": (c_int32, [cfgp, stp, c_int32, c_void_p, c_void_p, c_int64,
+                                            c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                            c_int32, c_int32, c_int32, c_void_p]),
         "hkv_check": (c_int32, [cfgp, stp, c_void_p]),
         "hkv_status_string": (ctypes.c_char_p, [c_int32]),
         "hkv_last_error": (ctypes.c_char_p, []),
@@ -209,6 +213,13 @@ def hkv_decode_step(cfg, state, t, k_new, v_new, ld_kv, q_win, ld_qw, out, ld_o,
     return _call("hkv_decode_step", ctypes.byref(cfg), ctypes.byref(state), t, _ptr(k_new),
                  _ptr(v_new), ld_kv, _ptr(q_win), ld_qw, _ptr(out), ld_o,
                  _ptr(evicted_pos_log), s_begin, s_count, _stream(stream))
+
+
+def hkv_decode_step_split(cfg, state, t, k_new, v_new, ld_kv, q_win, ld_qw, out, ld_o,
+                          evicted_pos_log, s_begin, s_count, n_split, stream=None):
+    return _call("hkv_decode_step_split", ctypes.byref(cfg), ctypes.byref(state), t,
+                 _ptr(k_new), _ptr(v_new), ld_kv, _ptr(q_win), ld_qw, _ptr(out), ld_o,
+                 _ptr(evicted_pos_log), s_begin, s_count, n_split, _stream(stream))
 
 
 def hkv_check(cfg, state, stream=None):

@@ -86,6 +86,8 @@ hkv_status derive(const hkv_config* c, Derived* d) {
   off = align256(off + size_t(d->pool_slots) * sizeof(int32_t));
   d->ws_keys = off;
   off = align256(off + size_t(d->pool_slots) * sizeof(uint64_t));
+  d->ws_part = off;
+  off = align256(off + size_t(S) * kMaxSplit * size_t(c->head_dim + 4) * sizeof(float));
   d->ws_bytes = off;
   return HKV_OK;
 }

@@ -15,6 +15,7 @@ constexpr int kMaxPrefill = 1024;   // classification keeps W x P logits on chip
 constexpr int kMaxWobs = 8;         // observation / scoring window queries
 constexpr int kMaxEvict = 8;        // evictions per decode event (M = W)
 constexpr int kMaxHeads = 1024;
+constexpr int kMaxSplit = 8;        // workgroups per stream in the split decode step
 
 struct Derived {
   int64_t S = 0;            // streams
@@ -27,6 +28,7 @@ struct Derived {
   size_t ws_tile = 0;          // float [pool_slots * w_obs]
   size_t ws_pos = 0;           // int32 [pool_slots]
   size_t ws_keys = 0;          // uint64 [pool_slots]
+  size_t ws_part = 0;          // float [S, kMaxSplit, head_dim + 4]: split partial states
   size_t ws_bytes = 0;
 };
 

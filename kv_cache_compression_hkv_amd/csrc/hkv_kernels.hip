@@ -128,7 +128,6 @@ struct CombineShared {
   float m[kNW];
   float l[kNW];
   float o[kNW][128];
-  float wm[kNW][kMaxWobs], wl[kNW][kMaxWobs];   // window-query softmax partials
 };
 
 struct EvictShared {
@@ -228,7 +227,9 @@ struct StepMfmaAttn {
 // Shape of the decode step per element type, head size and stream class C.
 // bf16 d128 has two: short streams (C = 0) run 8 waves/SIMD with 2 rows in
 // flight per lane, long streams (C = 1) 5 waves with 3; the host picks the class
-// from the configured budget.
+// from the configured budget.  C = 2 is the bf16 d64 eviction of the split
+// decode step, which has no matrix-core attention pass to take its tile from
+// and scores its slots from K like d128.
 //
 // How an eviction scores its slots, and how many its scratch holds on chip.
 // bf16 with the attention on the vector ALUs (kKeys): on the matrix cores, either
@@ -260,7 +261,7 @@ struct StepCfg {
       !kB16 ? HKV_U_F32 : (D == 64 ? HKV_U_B64 : (C ? HKV_U_B128L : HKV_U_B128S));
   static constexpr int kTilesInFlight = C ? HKV_UE_L : HKV_UE_S;
   static constexpr int kTilesInFlightRing = C ? HKV_UER_L : HKV_UER_S;
-  static constexpr bool kKeys = kB16 && !StepMfmaAttn<T, D>::value;
+  static constexpr bool kKeys = kB16 && (C == 2 || !StepMfmaAttn<T, D>::value);
   static constexpr int kOnePass = kKeys && !C ? HKV_ONEPASS_S : 0;
   static constexpr int kSlots =
       kKeys ? HKV_ONCHIP_KEYS : (kB16 ? HKV_ONCHIP_TILE_B16 : HKV_ONCHIP_TILE_F32);
@@ -280,6 +281,31 @@ struct QStage {
 #ifndef HKV_RING
 #define HKV_RING 1
 #endif
+
+// Softmax max and 1/sum of window queries 0 .. nq-1 over the slots each sees
+// (query i: position <= t - W + 1 + i), from the W x c logit tile; one wave per
+// query.  Kept out of line: it is the eviction's fallback when the ring of
+// query statistics is stale, and inlined it would cost the decode step
+// registers on every launch.
+__device__ __noinline__ void window_stats(const int* pos, const float* tile, int c, int t, int W,
+                                          int nq, float* qm, float* ql) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = wave; i < nq; i += kNW) {
+    const int lim = t - W + 1 + i;
+    float m = kNeg;
+    for (int j = lane; j < c; j += kWave)
+      if (pos[j] <= lim) m = fmaxf(m, tile[i * c + j]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int j = lane; j < c; j += kWave)
+      if (pos[j] <= lim) l += exp2f(tile[i * c + j] - m);
+    l = wave_sum(l);
+    if (lane == 0) {
+      qm[i] = m;
+      ql[i] = 1.0f / l;
+    }
+  }
+}
 
 template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
@@ -591,22 +617,28 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         }
       }
       __syncthreads();
-      // softmax statistics of each window query over the slots it sees
-      for (int i = wave; i < W; i += kNW) {
-        const int lim = t - W + 1 + i;
-        float m = kNeg;
-        for (int j = lane; j < c; j += kWave)
-          if (sc.pos[j] <= lim) m = fmaxf(m, sc.tile[i * c + j]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < c; j += kWave)
-          if (sc.pos[j] <= lim) l += exp2f(sc.tile[i * c + j] - m);
-        l = wave_sum(l);
-        if (lane == 0) {
-          es.qm[i] = m;
-          es.ql[i] = 1.0f / l;
+    }
+    // softmax statistics of each window query over the slots it sees.  With a
+    // tile from the attention the current query's came with it, and the
+    // earlier ones come from the ring when it is current (lanes i < W-1 of
+    // every wave read entry i, so every wave takes the same branch).
+    if (window) {
+      bool ring = false;
+      if (tile_ready && HKV_RING) {
+        bool ok = true;
+        float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lane < W - 1) {
+          const int step = t - W + 1 + lane;
+          e = a.qstat[(long long)s * W + step % W];
+          ok = __float_as_int(e.z) == step;
+        }
+        ring = __ballot(!ok) == 0;
+        if (ring && wave == 0 && lane < W - 1) {
+          es.qm[lane] = e.x;
+          es.ql[lane] = e.y;
         }
       }
+      if (!ring) window_stats(sc.pos, sc.tile, c, t, W, tile_ready ? W - 1 : W, es.qm, es.ql);
     }
     __syncthreads();            // tile, positions and window statistics complete
 
@@ -875,8 +907,6 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
   for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[kc][e] = 0.f;
-  // online softmax statistics of the window queries held in rows r < 3
-  float wm[3] = {kNeg, kNeg, kNeg}, wl[3] = {0.f, 0.f, 0.f};
 
   for (int tt = t0; tt < t1; tt += UT) {
     uint4 kb[UT][KC], vb[UT][KC];
@@ -925,17 +955,6 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
           if (i < W - 1) sc.tile[i * c + j] = S[r] * a.scale_log2;
         }
       }
-      if (due) {
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          const int i = lk * 3 + r;
-          const bool vis = valid && i < W - 1 && pv[u] <= a.t - W + 1 + i;
-          const float v = vis ? S[r] * a.scale_log2 : kNeg;
-          const float mn = fmaxf(wm[r], v);
-          wl[r] = wl[r] * exp2f(wm[r] - mn) + (vis ? exp2f(v - mn) : 0.f);
-          wm[r] = mn;
-        }
-      }
       const float sv = valid ? cur : kNeg;
       const float m_new = fmaxf(m_run, sv);
       const float alpha = exp2f(m_run - m_new);
@@ -971,22 +990,6 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
     if (lk == 0) {
       cs.m[wave] = m_w;
       cs.l[wave] = l_w;
-    }
-  }
-  if (due) {
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      float mm = wm[r];
-      mm = fmaxf(mm, dpp<0xB1>(mm));
-      mm = fmaxf(mm, dpp<0x4E>(mm));
-      mm = fmaxf(mm, dpp<0x141>(mm));
-      mm = fmaxf(mm, dpp<0x140>(mm));
-      const float ll = group_sum<16>(wl[r] * exp2f(wm[r] - mm));
-      const int i = lk * 3 + r;
-      if (li == 0 && i < W - 1) {
-        cs.wm[wave][i] = mm;
-        cs.wl[wave][i] = ll;
-      }
     }
   }
 }
@@ -1261,19 +1264,9 @@ void k_step(StepArgs a) {
     }
     cur_m = Mx;
     cur_il = 1.0f / L;
-    if (tile_here && tid < a.W) {        // statistics of window query tid
-      float Mq = Mx, Iq = cur_il;
-      if (tid != a.W - 1) {
-        Mq = kNeg;
-#pragma unroll
-        for (int w2 = 0; w2 < kNW; ++w2) Mq = fmaxf(Mq, cs.wm[w2][tid]);
-        float Lq = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < kNW; ++w2) Lq += cs.wl[w2][tid] * exp2f(cs.wm[w2][tid] - Mq);
-        Iq = 1.0f / Lq;
-      }
-      es.qm[tid] = Mq;
-      es.ql[tid] = Iq;
+    if (tile_here && tid == 0) {         // statistics of the current query
+      es.qm[a.W - 1] = Mx;
+      es.ql[a.W - 1] = cur_il;
     }
     if (AT && tid < D) {
       T* op = reinterpret_cast<T*>(a.out + ((long long)s * a.ld_o) * ES);
@@ -1307,6 +1300,285 @@ void k_step(StepArgs a) {
   if (tid == 0) {
     if (AP) a.count[s] = ext;
     if (glob && nf_final != nf0) a.n_free[s] = nf_final;
+  }
+}
+
+
+// ------------------------------------------------------------------ split decode step
+// The decode step of hkv_decode_step_split, for launches with few streams (one
+// layer of a model): k_split_attn spreads each stream's slots over n_split
+// workgroups that each leave a partial softmax state (max, sum, unnormalised
+// output) in the workspace, and k_combine_evict, launched after it on the same
+// stream, merges them into the output and runs the eviction of due streams.
+// The kernel boundary orders the two, so no device-scope fence is needed.
+// Split 0 also appends token t; the stream metadata (extent, free count) is
+// written back by the second kernel only, so every split reads the same values.
+struct StreamMeta {
+  long long base;
+  int lab, ext0, cap, B, nf0;
+  int ext, nf, slot_new, c;   // after the append of token t
+  bool glob, ok, full;        // full: append into a stream at capacity
+};
+
+// Metadata of stream s and the slot token t goes to (the rules of k_step).
+__device__ __forceinline__ StreamMeta stream_meta(const StepArgs& a, int s) {
+  StreamMeta m;
+  if (4LL * ((s >> 2) + 1) <= a.S)
+    m.lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
+  else
+    m.lab = a.label[s];
+  m.ext0 = a.count[s];
+  m.cap = a.cap[s];
+  m.B = a.budget[s];
+  m.base = a.base[s];
+  m.glob = m.lab == HKV_GLOBAL;
+  m.nf0 = m.glob ? a.n_free[s] : 0;
+  m.ext = m.ext0;
+  m.nf = m.nf0;
+  m.slot_new = -1;
+  m.full = false;
+  m.ok = m.nf0 >= 0 && m.nf0 <= a.M;
+  if (m.ok) {
+    if (m.lab == HKV_LOCAL) {
+      m.slot_new = a.t % m.B;
+      m.ext = m.ext0 + 1 < m.B ? m.ext0 + 1 : m.B;
+    } else if (m.nf0 > 0) {
+      m.slot_new = a.free_slots[(long long)s * a.M + (a.M - m.nf0)];
+      m.nf = m.nf0 - 1;
+      m.ok = m.slot_new >= 0 && m.slot_new < m.ext0;
+    } else {
+      m.slot_new = m.ext0;
+      m.ext = m.ext0 + 1;
+      if (m.ext0 >= m.cap) {
+        m.ok = false;
+        m.full = true;
+      }
+    }
+  }
+  m.c = m.ext - m.nf;
+  if (m.ok && (m.c < 1 || m.ext > m.cap || m.lab > HKV_FULL)) m.ok = false;
+  return m;
+}
+
+template <class T, int D, int C>
+__global__ __launch_bounds__(kNT)
+__attribute__((amdgpu_waves_per_eu(StepCfg<T, D, C>::kWaves, StepCfg<T, D, C>::kWaves)))
+void k_split_attn(StepArgs a, int n_split, float* part) {
+  using F = Frag<T>;
+  constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
+  constexpr int U = StepCfg<T, D, C>::kRows;
+  constexpr int PS = D + 4;                        // floats per partial state
+  __shared__ CombineShared cs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = xcd_block(blockIdx.x, gridDim.x);
+  const int s = a.s_begin + blk / n_split, p = blk % n_split;
+  const int g = lane / G, sub = lane % G;
+
+  const uint4 q_raw = ld16_once(a.q + ((long long)s * a.ld_q + sub * VE) * ES);
+  uint4 app = make_uint4(0, 0, 0, 0);
+  if (p == 0 && tid < 2 * G)
+    app = ld16_once((tid >= G ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + (tid % G) * VE) * ES);
+  const StreamMeta m = stream_meta(a, s);
+  if (!m.ok) return;                               // (reported by k_combine_evict)
+  const long long base = m.base;
+  const int ext = m.ext, nf = m.nf, slot_new = m.slot_new;
+  int fr[kMaxEvict];
+#pragma unroll
+  for (int k = 0; k < kMaxEvict; ++k)
+    fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
+  auto is_free = [&](int row) {
+    bool f = false;
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k) f |= (row == fr[k]);
+    return f;
+  };
+  if (p == 0) {                                    // append token t
+    if (tid < 2 * G) {
+      const bool isv = tid >= G;
+      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * D + (tid % G) * VE) * ES;
+      st16(dst, app);
+    }
+    if (tid == 0) {
+      a.pos[base + slot_new] = a.t;
+      if (m.glob) a.score[base + slot_new] = 0.0f;
+    }
+  }
+  // this split's share of the row tiles of [0, ext), then each wave's share
+  const int ntiles = (ext + R - 1) / R;
+  const int per_split = (ntiles + n_split - 1) / n_split;
+  const int s0 = min(ntiles, p * per_split), s1 = min(ntiles, s0 + per_split);
+  const int per = (s1 - s0 + kNW - 1) / kNW;
+  const int t0 = s0 + wave * per, t1 = min(s1, t0 + per);
+  // a stream that evicts at this step keeps its K rows in the caches for the
+  // eviction's pass over them
+  const bool keep_k = m.glob && m.c == m.B + a.M && a.q_win != nullptr;
+
+  float qv[VE];
+  {
+    float qf[VE];
+    F::to_f32(q_raw, qf);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) qv[i] = qf[i] * a.scale_log2;
+  }
+  const char* kbase = a.k_pool + (base * D + sub * VE) * ES;
+  const char* vbase = a.v_pool + (base * D + sub * VE) * ES;
+  const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
+  const char* vnew = a.v_new + ((long long)s * a.ld_kv + sub * VE) * ES;
+  float m_run = kNeg, l_run = 0.f;
+  float acc[VE];
+#pragma unroll
+  for (int i = 0; i < VE; ++i) acc[i] = 0.f;
+  for (int tt = t0; tt < t1; tt += U) {
+    uint4 kr[U], vr[U];
+    bool valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = (tt + u) * R + g;
+      valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
+      const int rr = valid[u] ? row : 0;
+      const bool fresh = rr == slot_new;
+      kr[u] = keep_k ? ld16(fresh ? knew : kbase + (long long)rr * D * ES)
+                     : ld16_stream(fresh ? knew : kbase + (long long)rr * D * ES);
+      vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * D * ES);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!valid[u]) {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float scr[U];
+    float m_tile = kNeg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VE];
+      F::to_f32(kr[u], kf);
+      float d0 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VE; ++i) d0 = fmaf(qv[i], kf[i], d0);
+      d0 = group_sum<G>(d0);
+      scr[u] = valid[u] ? d0 : kNeg;
+      m_tile = fmaxf(m_tile, scr[u]);
+    }
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pu = valid[u] ? exp2f(scr[u] - m_new) : 0.f;
+      l_run += pu;
+      float vf[VE];
+      F::to_f32(vr[u], vf);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[i] = fmaf(pu, vf[i], acc[i]);
+    }
+    m_run = m_new;
+  }
+  const float m_w = cross_group_max<G>(m_run);
+  const float f = exp2f(m_run - m_w);
+  l_run = cross_group_sum<G>(l_run * f);
+#pragma unroll
+  for (int i = 0; i < VE; ++i) acc[i] = cross_group_sum<G>(acc[i] * f);
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < VE; ++i) cs.o[wave][sub * VE + i] = acc[i];
+    if (sub == 0) {
+      cs.m[wave] = m_w;
+      cs.l[wave] = l_run;
+    }
+  }
+  __syncthreads();
+  float Mx = cs.m[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kNW; ++w2) Mx = fmaxf(Mx, cs.m[w2]);
+  float L = 0.f, o = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < kNW; ++w2) {
+    const float fw = exp2f(cs.m[w2] - Mx);
+    L = fmaf(cs.l[w2], fw, L);
+    if (tid < D) o = fmaf(cs.o[w2][tid], fw, o);
+  }
+  float* ps = part + ((long long)s * kMaxSplit + p) * PS;
+  if (tid < D) ps[tid] = o;
+  if (tid == 0) {
+    ps[D] = Mx;
+    ps[D + 1] = L;
+  }
+}
+
+template <class T, int D, int C>
+__global__ __launch_bounds__(kNT) void k_combine_evict(StepArgs a, int n_split, const float* part) {
+  using F = Frag<T>;
+  constexpr int ES = sizeof(T);
+  constexpr int CE = (sizeof(T) == 2 && D == 64) ? 2 : C;   // eviction shape
+  using OC = StepCfg<T, D, CE>;
+  constexpr int PS = D + 4;
+  __shared__ EvictShared es;
+  __shared__ uint64_t skeys[kNT];
+  __shared__ float lds_tile[!OC::kKeys ? kMaxWobs * OC::kSlots : 1];
+  __shared__ int lds_pos[OC::kKeys ? (OC::kOnePass ? OC::kOnePass : 1) : OC::kSlots];
+  __shared__ uint64_t lds_keys[OC::kKeys ? OC::kSlots : 1];
+  constexpr bool kQs = OC::kKeys;
+  __shared__ __align__(16) uint2 lds_qw[kQs ? kMaxWobs * QStage<D>::kPitch : 2];
+  const int tid = threadIdx.x;
+  const int s = a.s_begin + xcd_block(blockIdx.x, gridDim.x);
+
+  const StreamMeta m = stream_meta(a, s);
+  if (!m.ok) {
+    if (tid == 0) atomicOr(a.err, m.full ? (HKV_ERRBIT_CAPACITY | HKV_ERRBIT_LAYOUT) : HKV_ERRBIT_LAYOUT);
+    if (a.log && tid < a.M) a.log[(long long)s * a.M + tid] = -1;
+    return;
+  }
+  const bool due = m.glob && m.c == m.B + a.M;
+  if (due && tid < 2) es.cnt[tid] = 0;
+  // merge the partial states
+  const float* ps = part + (long long)s * kMaxSplit * PS;
+  float Mx = kNeg;
+  for (int q = 0; q < n_split; ++q) Mx = fmaxf(Mx, ps[q * PS + D]);
+  float L = 0.f, o = 0.f;
+  for (int q = 0; q < n_split; ++q) {
+    const float fw = exp2f(ps[q * PS + D] - Mx);
+    L = fmaf(ps[q * PS + D + 1], fw, L);
+    if (tid < D) o = fmaf(ps[q * PS + tid], fw, o);
+  }
+  const float cur_il = 1.0f / L;
+  if (tid < D) {
+    T* op = reinterpret_cast<T*>(a.out + ((long long)s * a.ld_o) * ES);
+    op[tid] = F::from_f32(o / L);
+  }
+  if (m.glob && tid == 0)
+    a.qstat[(long long)s * a.W + a.t % a.W] = make_float4(Mx, cur_il, __int_as_float(a.t), 0.f);
+  __syncthreads();                                 // subset counters zeroed
+  int nf_final = m.nf;
+  if (due) {
+    StepCtx x;
+    x.base = m.base;
+    x.s = s;
+    x.lab = m.lab;
+    x.c = m.c;
+    x.B = m.B;
+    x.slot_new = m.slot_new;
+    x.glob = m.glob;
+    x.due = due;
+    if (m.c <= OC::kSlots) {
+      Scratch sc{OC::kKeys ? reinterpret_cast<float*>(lds_keys) : lds_tile, lds_pos,
+                 OC::kKeys ? lds_keys : nullptr};
+      nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
+                                               Mx, cur_il);
+    } else {
+      Scratch sc{a.ws_tile + m.base * a.W, a.ws_pos + m.base, a.ws_keys + m.base};
+      nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
+                                               Mx, cur_il);
+    }
+  } else if (a.log && tid < a.M) {
+    a.log[(long long)s * a.M + tid] = -1;
+  }
+  if (tid == 0) {
+    a.count[s] = m.ext;
+    if (m.glob && nf_final != m.nf0) a.n_free[s] = nf_final;
   }
 }
 
@@ -1896,6 +2168,14 @@ void launch_step_t(const dev::StepArgs& a, int n, hipStream_t st) {
   hipLaunchKernelGGL((dev::k_step<T, D, C, AP, AT, EV>), dim3(n), dim3(dev::kNT), 0, st, a);
 }
 
+template <class T, int D, int C>
+void launch_split_t(const dev::StepArgs& a, int n, int n_split, float* part, hipStream_t st) {
+  hipLaunchKernelGGL((dev::k_split_attn<T, D, C>), dim3(n * n_split), dim3(dev::kNT), 0, st, a,
+                     n_split, part);
+  hipLaunchKernelGGL((dev::k_combine_evict<T, D, C>), dim3(n), dim3(dev::kNT), 0, st, a, n_split,
+                     static_cast<const float*>(part));
+}
+
 // Stream class of the bf16 d128 decode step: long streams (the uncompressed
 // layout, or a per-head budget above this many slots) keep more rows in flight
 // per wave; short ones run more waves.  Measured on MI355X.
@@ -1916,6 +2196,18 @@ void launch_step(const hkv_config* c, const dev::StepArgs& a, int n, hipStream_t
   } else {
     if (c->head_dim == 64) launch_step_t<float, 64, 0, AP, AT, EV>(a, n, st);
     else launch_step_t<float, 128, 0, AP, AT, EV>(a, n, st);
+  }
+}
+
+void launch_split(const hkv_config* c, const dev::StepArgs& a, int n, int n_split, float* part,
+                  hipStream_t st) {
+  if (c->dtype == HKV_DT_BF16) {
+    if (c->head_dim == 64) launch_split_t<uint16_t, 64, 0>(a, n, n_split, part, st);
+    else if (long_streams(c)) launch_split_t<uint16_t, 128, 1>(a, n, n_split, part, st);
+    else launch_split_t<uint16_t, 128, 0>(a, n, n_split, part, st);
+  } else {
+    if (c->head_dim == 64) launch_split_t<float, 64, 0>(a, n, n_split, part, st);
+    else launch_split_t<float, 128, 0>(a, n, n_split, part, st);
   }
 }
 
@@ -2284,6 +2576,44 @@ hkv_status hkv_decode_step(const hkv_config* c, hkv_state* st, int32_t t, const 
   a.s_begin = s_begin;
   launch_step<true, true, true>(c, a, s_count, static_cast<hipStream_t>(stream));
   return after_launch("k_step(fused)");
+}
+
+hkv_status hkv_decode_step_split(const hkv_config* c, hkv_state* st, int32_t t, const void* k_new,
+                                 const void* v_new, int64_t ld_kv, const void* q_win,
+                                 int64_t ld_qw, void* out, int64_t ld_o, int32_t* log,
+                                 int32_t s_begin, int32_t s_count, int32_t n_split, void* stream) {
+  Derived d;
+  hkv_status r = common_checks(c, st, t, s_begin, s_count, &d);
+  if (r != HKV_OK) return r;
+  if (n_split < 1 || n_split > kMaxSplit)
+    return fail(HKV_E_INVAL, "n_split %d outside [1, %d]", n_split, kMaxSplit);
+  const int eb = elem_bytes(c);
+  if ((r = check_data_ptr(k_new, ld_kv, eb, "k_new")) != HKV_OK) return r;
+  if ((r = check_data_ptr(v_new, ld_kv, eb, "v_new")) != HKV_OK) return r;
+  if ((r = check_data_ptr(q_win, ld_qw, eb, "q_win")) != HKV_OK) return r;
+  if (ld_qw < int64_t(c->w_obs) * c->head_dim)
+    return fail(HKV_E_INVAL, "ld_qw smaller than w_obs * head_dim");
+  if (!out) return fail(HKV_E_INVAL, "out is NULL");
+  if ((reinterpret_cast<uintptr_t>(out) & 3u) || ld_o < c->head_dim)
+    return fail(HKV_E_INVAL, "out misaligned or ld_o < head_dim");
+  if (log && (reinterpret_cast<uintptr_t>(log) & 3u))
+    return fail(HKV_E_INVAL, "evicted_pos_log misaligned");
+  if (s_count == 0) return HKV_OK;
+  dev::StepArgs a = step_args(c, st, d, t);
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.ld_kv = ld_kv;
+  a.q_win = static_cast<const char*>(q_win);
+  a.ld_qw = ld_qw;
+  a.q = a.q_win + (long long)(c->w_obs - 1) * c->head_dim * eb;   // newest query of the window
+  a.ld_q = ld_qw;
+  a.out = static_cast<char*>(out);
+  a.ld_o = ld_o;
+  a.log = log;
+  a.s_begin = s_begin;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(st->workspace) + d.ws_part);
+  launch_split(c, a, s_count, n_split, part, static_cast<hipStream_t>(stream));
+  return after_launch("k_split_attn/k_combine_evict");
 }
 
 hkv_status hkv_check(const hkv_config* c, const hkv_state* st, void* stream) {

@@ -75,7 +75,7 @@ def group_streams(w: HkvConfig, groups: Sequence[Tuple[int, int]]) -> List[int]:
 def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=None,
                    mode: str = "fused", inputs=None, cache=None,
                    per_layer: bool = False, prefill: bool = False,
-                   score_trace: bool = False, skip_attn=None) -> GpuRecord:
+                   score_trace: bool = False, skip_attn=None, n_split: int = 0) -> GpuRecord:
     """Classification and `steps` decode steps over ALL streams, in the layer-
     folded launch configuration (one call per entry point per step), or with
     per_layer one call per layer (its batch x heads streams) as a model runs.
@@ -84,7 +84,8 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
     score_trace the scores of the recorded streams' slots are read back after
     every step (an eviction writes the scores it ranked when given a log), for
     a comparison at every eviction event.  In mode "split", skip_attn(t) true
-    leaves out step t's attention call (its outputs are not compared)."""
+    leaves out step t's attention call (its outputs are not compared).  With
+    n_split > 0 the fused mode calls hkv_decode_step_split instead."""
     K, V, Q = inputs if inputs is not None else device_inputs(w, seed)
     cfg = hk.config_from_workload(w)
     cache = cache or hk.HkvCache(cfg)
@@ -123,13 +124,15 @@ def gpu_generation(w: HkvConfig, seed: int, streams: Sequence[int], *, steps=Non
         vp = V.data_ptr() + t * d * eb
         qp = Q.data_ptr() + (t - (P - W)) * d * eb          # query of position t
         qw = Q.data_ptr() + (t - W + 1 - (P - W)) * d * eb  # positions t-W+1 .. t
-        if mode == "fused" and per_layer:
-            per = w.batch * w.heads
-            for l in range(w.layers):
-                hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log,
-                                   l * per, per)
-        elif mode == "fused":
-            hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log, 0, S)
+        if mode == "fused":
+            per = w.batch * w.heads if per_layer else S
+            for s0 in range(0, S, per):
+                if n_split:
+                    hk.hkv_decode_step_split(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d,
+                                             log, s0, per, n_split)
+                else:
+                    hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log,
+                                       s0, per)
         else:
             hk.hkv_append(cfg, st, t, kp, vp, N * d, 0, S)
             if skip_attn is not None and skip_attn(t):

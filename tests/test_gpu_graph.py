@@ -22,12 +22,17 @@ def _state(cache):
              "budget", "base")}
 
 
-@pytest.mark.parametrize("kw", [dict(layers=3, batch=2),
-                                dict(layers=2, batch=2, dtype="f32", head_dim=128, heads=4,
-                                     rho=(1, 6), p_local=0.0)])
-def test_graph_replay_matches_eager(kw):
+@pytest.mark.parametrize("kw,n_split", [
+    (dict(layers=3, batch=2), 0),
+    (dict(layers=2, batch=2, dtype="f32", head_dim=128, heads=4, rho=(1, 6), p_local=0.0), 0),
+    # the split decode step (two kernels per layer per step)
+    (dict(layers=3, batch=2), 4),
+    (dict(layers=2, batch=2, head_dim=128, heads=6, image_tokens=744, prefill_image=100,
+          split_dist=60), 3),
+])
+def test_graph_replay_matches_eager(kw, n_split):
     w = small_config(**kw)
-    print(f"[gpu] graph replay {w.dtype} d={w.head_dim} S={w.S}", flush=True)
+    print(f"[gpu] graph replay {w.dtype} d={w.head_dim} S={w.S} n_split={n_split}", flush=True)
     K, V, Q = device_inputs(w, 5)
     cfg = hk.config_from_workload(w)
     cache = hk.HkvCache(cfg)
@@ -48,8 +53,12 @@ def test_graph_replay_matches_eager(kw):
             vp = V.data_ptr() + t * d * eb
             qw = Q.data_ptr() + (t - W + 1 - (P - W)) * d * eb
             for l in range(w.layers):
-                hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log,
-                                   l * per, per)
+                if n_split:
+                    hk.hkv_decode_step_split(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d,
+                                             log, l * per, per, n_split)
+                else:
+                    hk.hkv_decode_step(cfg, st, t, kp, vp, N * d, qw, w.q_rows * d, out, d, log,
+                                       l * per, per)
             outs[t - P].copy_(out)
             logs[t - P].copy_(log)
 

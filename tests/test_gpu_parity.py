@@ -372,3 +372,48 @@ def test_per_layer_launches_parity(kw):
           f"max err {rep.max_out_err:.3g}", flush=True)
     assert not rep.failures, rep.failures[:8]
     assert rep.events_checked > 0
+
+
+SPLIT_STEP_CASES = {
+    # (config, n_split): every element type and head size, stream classes, the
+    # d64 eviction on the keys route, workspace spill, ragged splits
+    "bf16_d64": (small_config(layers=3, batch=2), 3),
+    "bf16_d64_long_global": (small_config(heads=2, prefix=0, image_tokens=1500, prefill_image=64,
+                                          rho=(3, 4), split_dist=300, p_local=0.0), 8),
+    "bf16_d128_short": (small_config(head_dim=128, layers=2, rho=(1, 4), split_dist=20), 4),
+    "bf16_d128_long": (small_config(head_dim=128, heads=3, image_tokens=884, prefill_image=120,
+                                    split_dist=80, p_local=0.3), 5),
+    "bf16_d128_twopass_spill": (small_config(cid=44, head_dim=128, heads=8, image_tokens=1504,
+                                             prefill_image=100, rho=(1, 8), split_dist=60,
+                                             p_local=0.9), 8),
+    "f32_d64": (small_config(dtype="f32", heads=5), 2),
+    "f32_d128": (small_config(dtype="f32", head_dim=128, heads=3, rho=(1, 6), split_dist=40,
+                              p_local=0.0), 7),
+    "full_cache": (small_config(full_cache=True, image_tokens=120), 4),
+    "one_split": (small_config(layers=2), 1),
+    "ragged": (small_config(heads=7, prefix=5, image_tokens=143, prefill_image=37,
+                            local_window=13, split_dist=21, rho=(2, 7)), 6),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SPLIT_STEP_CASES))
+def test_parity_split_step_per_layer(name):
+    """hkv_decode_step_split, one launch pair per layer as a model runs it,
+    replayed on the oracle (every group, every step, lock-step scores)."""
+    w, n_split = SPLIT_STEP_CASES[name]
+    print(f"[gpu] split step per layer {name}: S={w.S} N={w.N} d={w.head_dim} "
+          f"n_split={n_split}", flush=True)
+    _check_all_groups(w, name, per_layer=True, n_split=n_split)
+
+
+def test_split_step_rejects_bad_split():
+    w = small_config()
+    cfg = hk.config_from_workload(w)
+    cache = hk.HkvCache(cfg)
+    cache.state.phase = 1
+    buf = torch.zeros((w.S, w.q_rows, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    for bad in (0, 9, -1):
+        with pytest.raises(hk.HkvError) as e:
+            hk.hkv_decode_step_split(cfg, cache.state, w.P, buf, buf, w.head_dim, buf,
+                                     w.q_rows * w.head_dim, buf, w.head_dim, None, 0, w.S, bad)
+        assert e.value.status == hk.E_INVAL
