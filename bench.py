@@ -425,6 +425,8 @@ def main():
                     help="also report the attention-output error against the full cache")
     ap.add_argument("--per-layer", action="store_true",
                     help="also time the per-layer decode loop, eager and as a HIP graph")
+    ap.add_argument("--per-layer-splits", default="2,4,8",
+                    help="n_split values of the split decode step timed with --per-layer")
     ap.add_argument("--prefill", action="store_true",
                     help="also time hkv_prefill (prefill attention with the classification as "
                          "its by-product) against hkv_classify")
@@ -488,7 +490,8 @@ def main():
         "labels": m["labels"],
     }
     if args.per_layer:
-        res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2))
+        splits = tuple(int(x) for x in args.per_layer_splits.split(",") if x)
+        res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2), splits)
     if args.prefill and w.dtype == "bf16":
         res["prefill"] = time_prefill(w, inputs, hk, full_cache_of)
     if not args.no_full_cache:
