@@ -425,6 +425,9 @@ def main():
                     help="also report the attention-output error against the full cache")
     ap.add_argument("--per-layer", action="store_true",
                     help="also time the per-layer decode loop, eager and as a HIP graph")
+    ap.add_argument("--jsonl", default="",
+                    help="also append the result, with a timestamp and the kernel sources' hash, "
+                         "to this JSONL file (a per-run log)")
     ap.add_argument("--per-layer-splits", default="2,4,8",
                     help="n_split values of the split decode step timed with --per-layer")
     ap.add_argument("--prefill", action="store_true",
@@ -533,7 +536,14 @@ def main():
                                    full_cache_of)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.seed)
-    print(json.dumps(res), flush=True)
+    line = json.dumps(res)
+    if args.jsonl:
+        # the run's record, appended with when and with which kernel sources it ran
+        rec = dict(res, time_utc=time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()),
+                   kernel_hash=kernel_hash(), argv=sys.argv[1:])
+        with open(args.jsonl, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    print(line, flush=True)
 
 
 if __name__ == "__main__":

@@ -1770,6 +1770,11 @@ struct PrefillArgs {
   float tau, scale_log2;
 };
 
+// Probabilities of the prefill's P.V product as two bf16 parts (1) or one (0).
+#ifndef HKV_PV_SPLIT
+#define HKV_PV_SPLIT 1
+#endif
+
 template <int D, int NWQ>
 __global__ __launch_bounds__(64 * NWQ) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void k_prefill(PrefillArgs a) {
@@ -1941,14 +1946,20 @@ void k_prefill(PrefillArgs a) {
     m = mn;
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] *= alpha;
-    // O^T += V^T P^T over 32 keys at a time: keys {2c*16 + lk*4 + e, (2c+1)*16 + lk*4 + e}
+    // O^T += V^T P^T over 32 keys at a time: keys {2c*16 + lk*4 + e, (2c+1)*16 + lk*4 + e}.
+    // The probabilities enter the matrix cores as bf16; with HKV_PV_SPLIT each is
+    // split into a bf16 high part and the bf16 rounding of the rest, two
+    // products, so that P carries about 16 bits instead of 8 (the output's error
+    // budget then goes to the bf16 rounding of the output alone)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      bf16x8 pb;
+      bf16x8 pb, pl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         pb[e] = __bf16(pr[2 * c][e]);
         pb[4 + e] = __bf16(pr[2 * c + 1][e]);
+        pl[e] = __bf16(pr[2 * c][e] - float(pb[e]));
+        pl[4 + e] = __bf16(pr[2 * c + 1][e] - float(pb[4 + e]));
       }
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
@@ -1958,6 +1969,9 @@ void k_prefill(PrefillArgs a) {
         const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
         o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb, o[t],
                                                        0, 0, 0);
+        if (HKV_PV_SPLIT)
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pl, o[t],
+                                                         0, 0, 0);
       }
     }
   }
