@@ -391,6 +391,30 @@ VARIANTS = {"headkv": (False, False), "unstratified": (True, False),
             "uniform_budget": (False, True), "uniform_unstratified": (True, True)}
 
 
+def copy_bandwidth(gib: int = 4, reps: int = 5) -> float:
+    """Achieved bandwidth of a plain device-to-device copy of `gib` GiB (bytes
+    read + written per second, best of `reps`): the practical HBM ceiling the
+    kernel's rate is also compared with."""
+    import torch
+    n = gib << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        best = max(best, 2.0 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    torch.cuda.empty_cache()
+    return best
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the HBM counters."""
     import torch
@@ -466,6 +490,7 @@ def main():
     tokens = w.batch * w.steps
     value = m["value"]
 
+    copy_gbs = copy_bandwidth()
     traffic = None
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
@@ -489,7 +514,9 @@ def main():
                      "traffic": traffic,
                      "kernel": "k_step (fused append + attention + STE)",
                      "mean_launch_us": m["mean_launch_us"],
-                     "alg_bytes_per_launch": m["alg_bytes_per_launch"]},
+                     "alg_bytes_per_launch": m["alg_bytes_per_launch"],
+                     "copy_GBs": round(copy_gbs, 1),
+                     "frac_of_copy": round(achieved / copy_gbs, 4)},
         "labels": m["labels"],
     }
     if args.per_layer:
