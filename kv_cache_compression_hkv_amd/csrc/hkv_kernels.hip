@@ -20,7 +20,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "hkv_device.h"
 #include "hkv_host.h"
@@ -122,6 +124,7 @@ struct StepArgs {
   int s_begin, t, w, W, M, D;
   int S;                               // streams in the state (label array length)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
+  int res64;                           // streams with s % 64 < res64 are resident
 };
 
 struct CombineShared {
@@ -182,6 +185,7 @@ struct StepCtx {
   long long base;
   int s, lab, c, B, slot_new;          // c: slots holding a token (no free slot when due)
   bool glob, due;
+  bool resident;                       // rows loaded with caching (kept across launches)
 };
 
 // Per-slot scratch of an eviction: the W x c logit tile and the positions, or
@@ -262,6 +266,8 @@ struct StepCfg {
   static constexpr int kTilesInFlight = C ? HKV_UE_L : HKV_UE_S;
   static constexpr int kTilesInFlightRing = C ? HKV_UER_L : HKV_UER_S;
   static constexpr bool kKeys = kB16 && (C == 2 || !StepMfmaAttn<T, D>::value);
+  // a share of the streams reads its rows with caching (decided per stream)
+  static constexpr bool kResident = kB16 && D == 128;
   static constexpr int kOnePass = kKeys && !C ? HKV_ONEPASS_S : 0;
   static constexpr int kSlots =
       kKeys ? HKV_ONCHIP_KEYS : (kB16 ? HKV_ONCHIP_TILE_B16 : HKV_ONCHIP_TILE_F32);
@@ -274,6 +280,21 @@ struct StepCfg {
 template <int D>
 struct QStage {
   static constexpr int kPitch = D / 4 + 2;   // row pitch in 8-byte units
+  // 8-byte units per thread: one, or two (16 bytes) when the workgroup has
+  // fewer threads than the W rows have 8-byte pieces
+  static constexpr int kPer = (kMaxWobs * D / 4 + kNT - 1) / kNT;
+  static_assert(kPer == 1 || kPer == 2, "one or two 8-byte pieces per thread");
+  using Piece = typename std::conditional<kPer == 1, uint2, uint4>::type;
+  // query row and 8-byte column of thread tid's piece
+  __device__ static int row(int tid) { return tid / (D / 4 / kPer); }
+  __device__ static int col(int tid) { return (tid % (D / 4 / kPer)) * kPer; }
+  // thread tid's piece of stream s's window queries (rows beyond W: not read)
+  __device__ static Piece load(const char* q_win, long long row0, int tid) {
+    return *reinterpret_cast<const Piece*>(q_win + (row0 + (long long)row(tid) * D + col(tid) * 4) * 2);
+  }
+  __device__ static void store(uint2* qs, int tid, Piece v) {
+    *reinterpret_cast<Piece*>(qs + row(tid) * kPitch + col(tid)) = v;
+  }
 };
 
 // Window statistics of an eviction taken from the query-statistics ring when
@@ -384,10 +405,8 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       constexpr int QP = QStage<D>::kPitch;
       if (!q_staged) {
         // (a standalone eviction stages the window queries here)
-        const int qrow = tid / (D / 4), qcol = tid % (D / 4);
-        if (qrow < W)
-          qs[qrow * QP + qcol] = *reinterpret_cast<const uint2*>(
-              a.q_win + ((long long)s * a.ld_qw + (long long)qrow * D + qcol * 4) * ES);
+        using QS = QStage<D>;
+        if (QS::row(tid) < W) QS::store(qs, tid, QS::load(a.q_win, (long long)s * a.ld_qw, tid));
         __syncthreads();
       }
       // A operand chunk kc of this lane: query row li, elements lk*8 + kc*32 .. +7,
@@ -867,7 +886,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
 // the W x c scoring tile comes out of the same instructions.  Lane l holds key
 // column l%16 and head elements (l/16)*8 + 32*kc .. +7 of K and V; softmax and
 // P.V run per lane on its column and are reduced over the 16 columns at the end.
-template <int D, bool AP>
+template <int D, bool AP, bool KC_>
 __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x, bool due,
                                             Scratch sc, CombineShared& cs) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -921,7 +940,7 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
       const char* vr = fresh ? vnew : a.v_pool + (base + jj) * D * ES;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        kb[u][kc] = ld16_stream(kr + (lk * 8 + kc * 32) * ES);
+        kb[u][kc] = KC_ ? ld16(kr + (lk * 8 + kc * 32) * ES) : ld16_stream(kr + (lk * 8 + kc * 32) * ES);
         vb[u][kc] = ld16_stream(vr + (lk * 8 + kc * 32) * ES);
       }
       pv[u] = 0;
@@ -994,12 +1013,85 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
   }
 }
 
+// The vector-ALU flash-decode loop over a stream's rows [t0, t1) of row tiles,
+// with its load policy fixed at compile time: a cache hint is part of the
+// load instruction, so a per-stream policy takes one copy of the loop each.
+// Invalid rows (ragged tail, freed slots) read row 0 and are zeroed, so all
+// fragments of a tile are in flight.  The same loop is written out inline in
+// k_step for the kernels with a launch-wide policy: called from there, the
+// bf16 d64 kernel spills (80 B, measured).
+template <class T, int D, int U, bool AP, bool cache_k, bool cache_v>
+__device__ __forceinline__ void rows_attend(int t0, int t1, int g, int ext, int nf, const int (&fr)[kMaxEvict],
+    int slot_new, const char* kbase, const char* vbase, const char* knew, const char* vnew,
+    const float (&qv)[Frag<T>::N], float& m_run, float& l_run, float (&acc)[Frag<T>::N]) {
+  using F = Frag<T>;
+  constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
+  auto is_free = [&](int row) {
+    bool f = false;
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k) f |= (row == fr[k]);
+    return f;
+  };
+    for (int tt = t0; tt < t1; tt += U) {
+    uint4 kr[U], vr[U];
+    bool valid[U];
+    // branch-free: an invalid row (ragged tail, freed slot) reads row 0 of
+    // the stream and is zeroed, so all fragments of the tile are in flight
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = (tt + u) * R + g;
+      valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
+      const int rr = valid[u] ? row : 0;
+      const bool fresh = AP && rr == slot_new;
+      const char* kp = fresh ? knew : kbase + (long long)rr * D * ES;
+      const char* vp = fresh ? vnew : vbase + (long long)rr * D * ES;
+      kr[u] = cache_k ? ld16(kp) : ld16_stream(kp);
+      vr[u] = cache_v ? ld16(vp) : ld16_stream(vp);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!valid[u]) {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float scr[U];
+    float m_tile = kNeg;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[VE];
+      F::to_f32(kr[u], kf);
+      float d0 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VE; ++i) d0 = fmaf(qv[i], kf[i], d0);
+      d0 = group_sum<G>(d0);
+      scr[u] = valid[u] ? d0 : kNeg;
+      m_tile = fmaxf(m_tile, scr[u]);
+    }
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = valid[u] ? exp2f(scr[u] - m_new) : 0.f;
+      l_run += p;
+      float vf[VE];
+      F::to_f32(vr[u], vf);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
+    }
+    m_run = m_new;
+  }
+}
+
 // ------------------------------------------------------------------ k_step
 // One workgroup per stream: append token t (optional), attend over the slots
 // present (optional) and, if the stream is a Global stream at B + M slots, evict
 // (optional) — one launch.  Every thread reads the stream's metadata itself
 // (uniform scalar loads, no barrier); the query is requested first.
-template <class T, int D, int C, bool AP, bool AT, bool EV>
+template <class T, int D, int C, bool AP, bool AT, bool EV, int KP>
 __global__ __launch_bounds__(kNT)
 __attribute__((amdgpu_waves_per_eu(StepCfg<T, D, C>::kWaves, StepCfg<T, D, C>::kWaves)))
 void k_step(StepArgs a) {
@@ -1020,7 +1112,6 @@ void k_step(StepArgs a) {
   __shared__ uint64_t lds_keys[EV && OC::kKeys ? OC::kSlots : 1];
   // window queries of a due bf16 stream whose score tile the eviction computes
   constexpr bool kQs = EV && sizeof(T) == 2 && !StepMfmaAttn<T, D>::value;
-  static_assert(!kQs || kMaxWobs * D / 4 <= kNT, "one 8-byte query piece per thread");
   __shared__ __align__(16) uint2 lds_qw[kQs ? kMaxWobs * QStage<D>::kPitch : 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s = a.s_begin + xcd_block(blockIdx.x, gridDim.x);
@@ -1129,6 +1220,14 @@ void k_step(StepArgs a) {
   x.slot_new = slot_new;
   x.glob = glob;
   x.due = due;
+  // a fixed share of the streams reads its rows with caching, the rest
+  // streams them past the caches: the resident share stays in the memory-side
+  // cache from one launch to the next, the streamed rows do not displace it
+  // KP: this launch keeps a share of its reads resident (per stream where
+  // OC::kResident, else all K rows)
+  constexpr bool kResShare = OC::kResident && KP != 0;
+  const bool resident = kResShare && (s & 63) < a.res64;
+  x.resident = resident;
 
   // ---------------- attention over slots [0, c)
   // With kMfma a bf16 Global stream at its eviction point (c == B + M) attends
@@ -1144,9 +1243,9 @@ void k_step(StepArgs a) {
     // (a standalone eviction runs the same pass and discards its output, so the
     // scores equal the fused step's bit for bit)
     if (onchip)
-      attend_mfma<D, AP>(a, x, tile_here, scr_l, cs);
+      attend_mfma<D, AP, KP != 0>(a, x, tile_here, scr_l, cs);
     else
-      attend_mfma<D, AP>(a, x, tile_here, scr_g, cs);
+      attend_mfma<D, AP, KP != 0>(a, x, tile_here, scr_g, cs);
   }
   if (AT && !mfma_pass) {
     float qv[VE];
@@ -1169,69 +1268,87 @@ void k_step(StepArgs a) {
     // the window queries of such a stream are fetched alongside its keys and
     // staged on chip after the loop
     const bool stage_q = kQs && keep_k;
-    const int qrow = tid / (D / 4), qcol = tid % (D / 4);
-    uint2 qw_raw = make_uint2(0, 0);
-    if (stage_q && qrow < a.W)
-      qw_raw = *reinterpret_cast<const uint2*>(
-          a.q_win + ((long long)s * a.ld_qw + (long long)qrow * D + qcol * 4) * ES);
+    using QS = QStage<D>;
+    typename QS::Piece qw_raw{};
+    if (stage_q && QS::row(tid) < a.W) qw_raw = QS::load(a.q_win, (long long)s * a.ld_qw, tid);
 
     float m_run = kNeg, l_run = 0.f;
     float acc[VE];
 #pragma unroll
     for (int i = 0; i < VE; ++i) acc[i] = 0.f;
 
-    for (int tt = t0; tt < t1; tt += U) {
-      uint4 kr[U], vr[U];
-      bool valid[U];
-      // branch-free: an invalid row (ragged tail, freed slot) reads row 0 of
-      // the stream and is zeroed, so all fragments of the tile are in flight
+    // load policy: K is cached for a resident stream, for a launch that keeps
+    // all K rows resident, and for an eviction that reads K again; V only for a
+    // resident stream; everything else is streamed
+    if constexpr (kResShare) {
+      // resident streams, eviction-point streams (K read again) and the rest
+      if (resident)
+        rows_attend<T, D, U, AP, true, true>(t0, t1, g, ext, nf, fr, slot_new, kbase, vbase, knew,
+                                             vnew, qv, m_run, l_run, acc);
+      else if (keep_k)
+        rows_attend<T, D, U, AP, true, false>(t0, t1, g, ext, nf, fr, slot_new, kbase, vbase, knew,
+                                              vnew, qv, m_run, l_run, acc);
+      else
+        rows_attend<T, D, U, AP, false, false>(t0, t1, g, ext, nf, fr, slot_new, kbase, vbase,
+                                               knew, vnew, qv, m_run, l_run, acc);
+    } else {
+      // one policy for the launch: K cached when the launch keeps all K rows
+      // resident (or, fp32, for an eviction that reads K again), V streamed
+      const bool cache_k = (KP && !OC::kResident) || (!kMfma && keep_k);
+      for (int tt = t0; tt < t1; tt += U) {
+        uint4 kr[U], vr[U];
+        bool valid[U];
+        // branch-free: an invalid row (ragged tail, freed slot) reads row 0 of
+        // the stream and is zeroed, so all fragments of the tile are in flight
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = (tt + u) * R + g;
-        valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
-        const int rr = valid[u] ? row : 0;
-        const bool fresh = AP && rr == slot_new;
-        kr[u] = keep_k ? ld16(fresh ? knew : kbase + (long long)rr * D * ES)
-                       : ld16_stream(fresh ? knew : kbase + (long long)rr * D * ES);
-        vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * D * ES);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (!valid[u]) {
-          kr[u] = make_uint4(0, 0, 0, 0);
-          vr[u] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+          const int row = (tt + u) * R + g;
+          valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
+          const int rr = valid[u] ? row : 0;
+          const bool fresh = AP && rr == slot_new;
+          const char* kp = fresh ? knew : kbase + (long long)rr * D * ES;
+          const char* vp = fresh ? vnew : vbase + (long long)rr * D * ES;
+          kr[u] = cache_k ? ld16(kp) : ld16_stream(kp);
+          vr[u] = ld16_stream(vp);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (!valid[u]) {
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = make_uint4(0, 0, 0, 0);
+          }
+        }
+        float scr[U];
+        float m_tile = kNeg;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float kf[VE];
+          F::to_f32(kr[u], kf);
+          float d0 = 0.f;
+#pragma unroll
+          for (int i = 0; i < VE; ++i) d0 = fmaf(qv[i], kf[i], d0);
+          d0 = group_sum<G>(d0);
+          scr[u] = valid[u] ? d0 : kNeg;
+          m_tile = fmaxf(m_tile, scr[u]);
+        }
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = valid[u] ? exp2f(scr[u] - m_new) : 0.f;
+          l_run += p;
+          float vf[VE];
+          F::to_f32(vr[u], vf);
+#pragma unroll
+          for (int i = 0; i < VE; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
+        }
+        m_run = m_new;
       }
-      float scr[U];
-      float m_tile = kNeg;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float kf[VE];
-        F::to_f32(kr[u], kf);
-        float d0 = 0.f;
-#pragma unroll
-        for (int i = 0; i < VE; ++i) d0 = fmaf(qv[i], kf[i], d0);
-        d0 = group_sum<G>(d0);
-        scr[u] = valid[u] ? d0 : kNeg;
-        m_tile = fmaxf(m_tile, scr[u]);
-      }
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < VE; ++i) acc[i] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = valid[u] ? exp2f(scr[u] - m_new) : 0.f;
-        l_run += p;
-        float vf[VE];
-        F::to_f32(vr[u], vf);
-#pragma unroll
-        for (int i = 0; i < VE; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
-      }
-      m_run = m_new;
     }
-    if (stage_q && qrow < a.W) lds_qw[qrow * QStage<D>::kPitch + qcol] = qw_raw;
+    if (stage_q && QS::row(tid) < a.W) QS::store(lds_qw, tid, qw_raw);
     // combine the R groups of the wave
     const float m_w = cross_group_max<G>(m_run);
     const float f = exp2f(m_run - m_w);
@@ -2177,9 +2294,44 @@ hkv_status after_launch(const char* what) {
   return e == hipSuccess ? HKV_OK : hip_fail(e, what);
 }
 
-template <class T, int D, int C, bool AP, bool AT, bool EV>
+
+// Residency of the decode step's reads in the memory-side cache (the 256 MB
+// Infinity Cache in front of HBM).  Each step reads every cached row once, in
+// the same order, and the pool is larger than that cache: loaded with default
+// caching, the rows would evict each other before the next step comes back to
+// them.  So rows are streamed past the caches (non-temporal loads), except for
+// a fixed share of about kResidentBytes that is loaded with caching every step
+// and so is found in the cache by the next one.  bf16 d128 takes the share per
+// stream (streams with s % 64 < res64); bf16 d64 all K rows or none, whichever
+// is nearer the target (a per-stream choice costs that kernel registers it
+// does not have).  The byte target was measured on MI355X: about 140-210 MB
+// helped every workload, more thrashes.  HKV_RESIDENT_MB overrides it (0:
+// stream everything).
+struct Residency {
+  int res64 = 0;        // bf16 d128: resident share of the streams, in 64ths
+  bool cache_k = false; // bf16 d64: K rows loaded with caching
+};
+
+Residency residency(const hkv_config* c, const Derived& d) {
+  static const double target = [] {
+    const char* e = getenv("HKV_RESIDENT_MB");
+    return (e ? atof(e) : 140.0) * double(1 << 20);
+  }();
+  Residency r;
+  if (c->dtype != HKV_DT_BF16 || target <= 0.0) return r;
+  const double kv_bytes = double(d.pool_slots) * 2.0 * c->head_dim * 2.0;   // K and V rows
+  if (c->head_dim == 128) {
+    const double share = std::floor(64.0 * target / kv_bytes + 0.5);
+    r.res64 = share > 64.0 ? 64 : int(share);
+  } else {
+    r.cache_k = kv_bytes / 2.0 < 2.0 * target;
+  }
+  return r;
+}
+
+template <class T, int D, int C, bool AP, bool AT, bool EV, int KP = 0>
 void launch_step_t(const dev::StepArgs& a, int n, hipStream_t st) {
-  hipLaunchKernelGGL((dev::k_step<T, D, C, AP, AT, EV>), dim3(n), dim3(dev::kNT), 0, st, a);
+  hipLaunchKernelGGL((dev::k_step<T, D, C, AP, AT, EV, KP>), dim3(n), dim3(dev::kNT), 0, st, a);
 }
 
 template <class T, int D, int C>
@@ -2202,11 +2354,27 @@ bool long_streams(const hkv_config* c) {
 }
 
 template <bool AP, bool AT, bool EV>
-void launch_step(const hkv_config* c, const dev::StepArgs& a, int n, hipStream_t st) {
+void launch_step(const hkv_config* c, const dev::StepArgs& a0, int n, hipStream_t st) {
+  // the resident share pays off in a launch over every stream; a launch over a
+  // part of them (one layer of a model run layer by layer) is bound by its
+  // workgroups' latency and measured slower with it
+  Derived d;
+  derive(c, &d);
+  const Residency r = n == d.S ? residency(c, d) : Residency{};
+  dev::StepArgs a = a0;
+  a.res64 = r.res64;
   if (c->dtype == HKV_DT_BF16) {
-    if (c->head_dim == 64) launch_step_t<uint16_t, 64, 0, AP, AT, EV>(a, n, st);
-    else if (long_streams(c)) launch_step_t<uint16_t, 128, 1, AP, AT, EV>(a, n, st);
-    else launch_step_t<uint16_t, 128, 0, AP, AT, EV>(a, n, st);
+    if (c->head_dim == 64) {
+      if (r.cache_k) launch_step_t<uint16_t, 64, 0, AP, AT, EV, 1>(a, n, st);
+      else launch_step_t<uint16_t, 64, 0, AP, AT, EV, 0>(a, n, st);
+    }
+    else if (long_streams(c)) {
+      if (r.res64) launch_step_t<uint16_t, 128, 1, AP, AT, EV, 1>(a, n, st);
+      else launch_step_t<uint16_t, 128, 1, AP, AT, EV, 0>(a, n, st);
+    } else {
+      if (r.res64) launch_step_t<uint16_t, 128, 0, AP, AT, EV, 1>(a, n, st);
+      else launch_step_t<uint16_t, 128, 0, AP, AT, EV, 0>(a, n, st);
+    }
   } else {
     if (c->head_dim == 64) launch_step_t<float, 64, 0, AP, AT, EV>(a, n, st);
     else launch_step_t<float, 128, 0, AP, AT, EV>(a, n, st);
@@ -2253,6 +2421,7 @@ dev::StepArgs step_args(const hkv_config* c, hkv_state* st, const Derived& d, in
   a.D = d.split;
   a.scale_log2 = scale_log2_of(c->head_dim);
   a.S = int(d.S);
+  a.res64 = 0;                         // set per launch (launch_step)
   return a;
 }
 
