@@ -1144,27 +1144,37 @@ void k_step(StepArgs a) {
   if (AP && tid < 2 * G)
     app = ld16_once((tid >= G ? a.v_new : a.k_new) + ((long long)s * a.ld_kv + (tid % G) * VE) * ES);
 
-  // the label byte through the scalar path (aligned 32-bit word), except in a
-  // last partial word
-  int lab;
-  if (4LL * ((s >> 2) + 1) <= a.S)
-    lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
-  else
-    lab = a.label[s];
+  // Stream metadata.  Every load is issued before the first wait (scalar loads
+  // return out of order, so a wait is for all of them): none depends on
+  // another, and a stream that needs fewer discards the rest.  The free-list
+  // row is read whole (entries past M repeat the last one); the label byte
+  // through the vector path (no scalar byte load), so no branch separates it
+  // from the others.
   const int ext0 = a.count[s];               // table extent (slots in use incl. freed)
   const int capv = a.cap[s];
   const int B = a.budget[s];
   const long long base = a.base[s];
+  const int nf_raw = a.n_free[s];
+  int fl[kMaxEvict];
+  {
+    const int last = (a.M > 0 ? a.M : 1) - 1;
+    const int* row = a.free_slots + (long long)s * a.M;
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k) fl[k] = row[k < last ? k : last];
+  }
+  const int lab = a.label[s];
   const bool glob = lab == HKV_GLOBAL;
-  const int nf0 = glob ? a.n_free[s] : 0;    // freed slots not yet refilled
+  const int nf0 = glob ? nf_raw : 0;         // freed slots not yet refilled
   int ext = ext0, nf = nf0, slot_new = -1;
   bool ok = nf0 >= 0 && nf0 <= a.M;
   if (ok && AP) {
     if (lab == HKV_LOCAL) {                   // ring of B slots (B = w, or A)
       slot_new = a.t % B;
       ext = ext0 + 1 < B ? ext0 + 1 : B;
-    } else if (nf0 > 0) {                     // lowest freed slot
-      slot_new = a.free_slots[(long long)s * a.M + (a.M - nf0)];
+    } else if (nf0 > 0) {                     // lowest freed slot: entry M - nf0
+#pragma unroll
+      for (int k = 0; k < kMaxEvict; ++k)
+        if (k == a.M - nf0) slot_new = fl[k];
       nf = nf0 - 1;
       ok = slot_new >= 0 && slot_new < ext0;
     } else {
@@ -1184,24 +1194,10 @@ void k_step(StepArgs a) {
     return;
   }
   const bool due = EV && glob && (c == B + a.M);
-  // freed slots still empty: the last nf entries of the stream's free list
+  // freed slots still empty: entries M - nf .. M - 1 of the free list
   int fr[kMaxEvict];
-  static_assert(kMaxEvict <= kWave, "one free-list entry per lane");
-  if constexpr (sizeof(T) == 2 && !kMfma) {
-    // (scalar registers: the d128 kernel's vector registers are the scarce ones)
 #pragma unroll
-    for (int k = 0; k < kMaxEvict; ++k) fr[k] = -1;
-    if (nf > 0) {
-      // one load: lane k fetches entry k, then every entry moves to a scalar register
-      const int frl = lane < nf ? a.free_slots[(long long)s * a.M + (a.M - nf) + lane] : -1;
-#pragma unroll
-      for (int k = 0; k < kMaxEvict; ++k) fr[k] = __builtin_amdgcn_readlane(frl, k);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kMaxEvict; ++k)
-      fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
-  }
+  for (int k = 0; k < kMaxEvict; ++k) fr[k] = (k >= a.M - nf && k < a.M) ? fl[k] : -1;
   auto is_free = [&](int row) {
     bool f = false;
 #pragma unroll
@@ -1452,21 +1448,27 @@ struct StreamMeta {
   int lab, ext0, cap, B, nf0;
   int ext, nf, slot_new, c;   // after the append of token t
   bool glob, ok, full;        // full: append into a stream at capacity
+  int fl[kMaxEvict];          // the free-list row (entries past M repeat the last)
 };
 
 // Metadata of stream s and the slot token t goes to (the rules of k_step).
 __device__ __forceinline__ StreamMeta stream_meta(const StepArgs& a, int s) {
+  // every load issued before the first wait, as in k_step
   StreamMeta m;
-  if (4LL * ((s >> 2) + 1) <= a.S)
-    m.lab = int((reinterpret_cast<const uint32_t*>(a.label)[s >> 2] >> ((s & 3) * 8)) & 0xffu);
-  else
-    m.lab = a.label[s];
   m.ext0 = a.count[s];
   m.cap = a.cap[s];
   m.B = a.budget[s];
   m.base = a.base[s];
+  const int nf_raw = a.n_free[s];
+  {
+    const int last = (a.M > 0 ? a.M : 1) - 1;
+    const int* row = a.free_slots + (long long)s * a.M;
+#pragma unroll
+    for (int k = 0; k < kMaxEvict; ++k) m.fl[k] = row[k < last ? k : last];
+  }
+  m.lab = a.label[s];
   m.glob = m.lab == HKV_GLOBAL;
-  m.nf0 = m.glob ? a.n_free[s] : 0;
+  m.nf0 = m.glob ? nf_raw : 0;
   m.ext = m.ext0;
   m.nf = m.nf0;
   m.slot_new = -1;
@@ -1477,7 +1479,9 @@ __device__ __forceinline__ StreamMeta stream_meta(const StepArgs& a, int s) {
       m.slot_new = a.t % m.B;
       m.ext = m.ext0 + 1 < m.B ? m.ext0 + 1 : m.B;
     } else if (m.nf0 > 0) {
-      m.slot_new = a.free_slots[(long long)s * a.M + (a.M - m.nf0)];
+#pragma unroll
+      for (int k = 0; k < kMaxEvict; ++k)
+        if (k == a.M - m.nf0) m.slot_new = m.fl[k];
       m.nf = m.nf0 - 1;
       m.ok = m.slot_new >= 0 && m.slot_new < m.ext0;
     } else {
@@ -1518,8 +1522,7 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
   const int ext = m.ext, nf = m.nf, slot_new = m.slot_new;
   int fr[kMaxEvict];
 #pragma unroll
-  for (int k = 0; k < kMaxEvict; ++k)
-    fr[k] = (k < nf) ? a.free_slots[(long long)s * a.M + (a.M - nf) + k] : -1;
+  for (int k = 0; k < kMaxEvict; ++k) fr[k] = (k >= a.M - nf && k < a.M) ? m.fl[k] : -1;
   auto is_free = [&](int row) {
     bool f = false;
 #pragma unroll
