@@ -356,6 +356,9 @@ def test_empty_range_and_phase():
 
 
 @pytest.mark.parametrize("kw", [dict(layers=3, batch=2),
+                                # bf16 d128, budgets 104 and 190 (short-stream class)
+                                dict(layers=2, batch=2, head_dim=128, heads=6, image_tokens=400,
+                                     prefill_image=100, split_dist=60),
                                 dict(layers=2, batch=2, head_dim=128, heads=6, image_tokens=744,
                                      prefill_image=100, split_dist=60)])
 def test_per_layer_launches_parity(kw):
