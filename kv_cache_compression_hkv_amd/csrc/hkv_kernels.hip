@@ -147,6 +147,7 @@ struct CombineShared {
 };
 
 struct EvictShared {
+  float4 ring[kMaxWobs];               // the stream's query-statistics ring, staged (bf16 d64)
   int cnt[2];
   float qm[kMaxWobs], ql[kMaxWobs];    // softmax max / 1/sum of each window query
   float pm[kNW][kMaxWobs], pl[kNW][kMaxWobs];   // per-wave partials of the tile pass
@@ -349,11 +350,12 @@ template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
                                             EvictShared& es, uint64_t* skeys, bool tile_ready,
                                             uint2* qs, bool q_staged, bool cur_known,
-                                            float cur_m, float cur_il) {
+                                            float cur_m, float cur_il, const float4* ring_lds) {
   // (returns the number of freed slots: M, or 0 if nothing was evicted; skeys:
   // on-chip room for kNT keys, free once the eviction starts; es.cnt zeroed
   // by the caller before a barrier; cur_known: this launch's attention gave
-  // the current query's softmax max cur_m and 1/sum cur_il)
+  // the current query's softmax max cur_m and 1/sum cur_il; ring_lds: the
+  // stream's ring row staged on chip before a barrier, or null)
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -665,7 +667,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
         float4 e = make_float4(0.f, 0.f, 0.f, 0.f);
         if (lane < W - 1) {
           const int step = t - W + 1 + lane;
-          e = a.qstat[(long long)s * W + step % W];
+          e = ring_lds ? ring_lds[step % W] : a.qstat[(long long)s * W + step % W];
           ok = __float_as_int(e.z) == step;
         }
         ring = __ballot(!ok) == 0;
@@ -1163,6 +1165,13 @@ void k_step(StepArgs a) {
     for (int k = 0; k < kMaxEvict; ++k) fl[k] = row[k < last ? k : last];
   }
   const int lab = a.label[s];
+  // bf16 d64: the stream's ring of window-query statistics (what its eviction
+  // scores with) comes with the metadata and is staged on chip below, so the
+  // eviction does not wait on a load of its own.  (At d128 the registers it
+  // holds meanwhile cost more than the wait: measured on MI355X.)
+  constexpr bool kRingStaged = EV && AT && kMfma;
+  float4 ring_raw = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (kRingStaged) ring_raw = a.qstat[(long long)s * a.W + min(lane & 7, a.W - 1)];
   const bool glob = lab == HKV_GLOBAL;
   const int nf0 = glob ? nf_raw : 0;         // freed slots not yet refilled
   int ext = ext0, nf = nf0, slot_new = -1;
@@ -1194,6 +1203,8 @@ void k_step(StepArgs a) {
     return;
   }
   const bool due = EV && glob && (c == B + a.M);
+  if constexpr (kRingStaged)                  // (read after the combine's barrier)
+    if (wave == 0 && lane < a.W) es.ring[lane] = ring_raw;
   // freed slots still empty: entries M - nf .. M - 1 of the free list
   int fr[kMaxEvict];
 #pragma unroll
@@ -1418,10 +1429,10 @@ void k_step(StepArgs a) {
       uint64_t* skeys = reinterpret_cast<uint64_t*>(&cs.o[0][0]);
       if (onchip)
         nf_final = evict_stream<T, D, C, AP>(a, x, scr_l, es, skeys, ready, lds_qw, q_staged, AT,
-                                             cur_m, cur_il);
+                                             cur_m, cur_il, kRingStaged ? es.ring : nullptr);
       else
         nf_final = evict_stream<T, D, C, AP>(a, x, scr_g, es, skeys, ready, lds_qw, q_staged, AT,
-                                             cur_m, cur_il);
+                                             cur_m, cur_il, kRingStaged ? es.ring : nullptr);
     } else if (a.log && tid < a.M) {
       a.log[(long long)s * a.M + tid] = -1;
     }
@@ -1704,11 +1715,11 @@ __global__ __launch_bounds__(kNT) void k_combine_evict(StepArgs a, int n_split, 
       Scratch sc{OC::kKeys ? reinterpret_cast<float*>(lds_keys) : lds_tile, lds_pos,
                  OC::kKeys ? lds_keys : nullptr};
       nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
-                                               Mx, cur_il);
+                                               Mx, cur_il, nullptr);
     } else {
       Scratch sc{a.ws_tile + m.base * a.W, a.ws_pos + m.base, a.ws_keys + m.base};
       nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
-                                               Mx, cur_il);
+                                               Mx, cur_il, nullptr);
     }
   } else if (a.log && tid < a.M) {
     a.log[(long long)s * a.M + tid] = -1;
