@@ -250,7 +250,13 @@ hkv_status hkv_ste_evict(const hkv_config *cfg, hkv_state *st, int32_t t,
  * token, the head attends over what it keeps, and a Global head at its budget
  * runs Stratified Token Eviction.  Arguments, layouts and errors are those of
  * the three calls; k_new/v_new rows at ptr + s*ld_kv, the W-query window at
- * q_win + s*ld_qw (oldest first), out at out + s*ld_o. */
+ * q_win + s*ld_qw (oldest first), out at out + s*ld_o.
+ * Performance only (results do not depend on it): a launch over every stream
+ * reads a fixed share of the pool, about 140 MiB, with default caching and the
+ * rest with non-temporal loads, so that the share stays in the GPU's
+ * memory-side cache from one step to the next; the environment variable
+ * HKV_RESIDENT_MB, read once per process, sets that size (0: none).  A launch
+ * over part of the streams streams everything. */
 hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
                            const void *k_new, const void *v_new, int64_t ld_kv,
                            const void *q_win, int64_t ld_qw, void *out, int64_t ld_o,
