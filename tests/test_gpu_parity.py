@@ -38,6 +38,8 @@ CASES = {
     "wide_window": small_config(local_window=44, p_local=1.0),
     # uncompressed baseline layout
     "full_cache": small_config(full_cache=True, image_tokens=120),
+    # a full-cache layout evicts nothing: M = 0 is valid there, and its free list is empty
+    "full_cache_m0": small_config(full_cache=True, image_tokens=120, evict_m=0),
     # uncompressed layout with a prefill beyond the classification's on-chip
     # limit of 1024 positions (the full layout needs no classification)
     "full_cache_long_prefill": small_config(full_cache=True, image_tokens=1200,
