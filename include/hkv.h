@@ -120,7 +120,8 @@ typedef struct {
   int32_t *budget;            /* [S] w (Local), B_g (Global), N (full)         */
   int32_t *n_tokens;          /* [S] classification count                      */
   uint8_t *label;             /* [S] hkv_label (4-byte aligned)                */
-  int32_t *free_slots;        /* [S, M] slots freed by the last eviction       */
+  int32_t *free_slots;        /* [S, max(M, 1)] slots freed by the last eviction
+                                 (the decode step reads a row whatever the label) */
   int32_t *n_free;            /* [S] of those, how many are still free         */
   float   *qstat;             /* [S, w_obs, 4] per Global stream, the softmax
                                * statistics of its last w_obs decode queries:

@@ -1159,10 +1159,8 @@ void k_step(StepArgs a) {
   const int nf_raw = a.n_free[s];
   int fl[kMaxEvict];
   {
-    // (with M = 0, a full-cache layout without evictions, the free list may
-    // be empty: the reads then go to the stream's extent, and go unused)
     const int last = (a.M > 0 ? a.M : 1) - 1;
-    const int* row = a.M > 0 ? a.free_slots + (long long)s * a.M : a.count + s;
+    const int* row = a.free_slots + (long long)s * a.M;
 #pragma unroll
     for (int k = 0; k < kMaxEvict; ++k) fl[k] = row[k < last ? k : last];
   }
@@ -1474,10 +1472,8 @@ __device__ __forceinline__ StreamMeta stream_meta(const StepArgs& a, int s) {
   m.base = a.base[s];
   const int nf_raw = a.n_free[s];
   {
-    // (with M = 0, a full-cache layout without evictions, the free list may
-    // be empty: the reads then go to the stream's extent, and go unused)
     const int last = (a.M > 0 ? a.M : 1) - 1;
-    const int* row = a.M > 0 ? a.free_slots + (long long)s * a.M : a.count + s;
+    const int* row = a.free_slots + (long long)s * a.M;
 #pragma unroll
     for (int k = 0; k < kMaxEvict; ++k) m.fl[k] = row[k < last ? k : last];
   }
