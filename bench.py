@@ -12,13 +12,15 @@ head_dim 64, N = 696, P = 184, rho = 1/6 (512 decode steps).
 
 Prints ONE JSON line.  value = generated tokens per second = batch * decode
 steps / step time.  The roofline block is for the dominant kernel (the fused
-decode step): algorithmic bytes per launch / mean launch time from HIP events
-recorded around every launch inside the timed region.
+decode step): algorithmic bytes per launch / mean launch time, from HIP events
+recorded on the launch stream around each timed generation's decode loop and
+divided by its launches.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -35,11 +37,18 @@ KERNEL_SOURCES = ("kv_cache_compression_hkv_amd/csrc/hkv_kernels.hip",
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hkv_decode_step_llamagen_xl_counters.json")
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/', re.S)
+
+
 def kernel_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace do not count,
+    so a recorded counter run stays valid until the code itself changes."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        code = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

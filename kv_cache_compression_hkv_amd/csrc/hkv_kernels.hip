@@ -2338,8 +2338,8 @@ hkv_status after_launch(const char* what) {
 // the same order, and the pool is larger than that cache: loaded with default
 // caching, the rows would evict each other before the next step comes back to
 // them.  So rows are streamed past the caches (non-temporal loads), except for
-// a fixed share of about kResidentBytes that is loaded with caching every step
-// and so is found in the cache by the next one.  bf16 d128 takes the share per
+// a fixed share of about 140 MiB that is loaded with caching every step and so
+// is found in the cache by the next one.  bf16 d128 takes the share per
 // stream (streams with s % 64 < res64); bf16 d64 all K rows or none, whichever
 // is nearer the target (a per-stream choice costs that kernel registers it
 // does not have).  The byte target was measured on MI355X: about 140-210 MB
