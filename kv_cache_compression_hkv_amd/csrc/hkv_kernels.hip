@@ -40,7 +40,7 @@ namespace dev {
 #define HKV_U_B64 4
 #endif
 #ifndef HKV_U_B128S            // bf16 d128, short streams
-#define HKV_U_B128S 2
+#define HKV_U_B128S 3
 #endif
 #ifndef HKV_U_B128L            // bf16 d128, long streams
 #define HKV_U_B128L 3
@@ -58,7 +58,7 @@ namespace dev {
 #define HKV_WPE_B64 6
 #endif
 #ifndef HKV_WPE_B128S
-#define HKV_WPE_B128S 8
+#define HKV_WPE_B128S 7
 #endif
 #ifndef HKV_WPE_B128L
 #define HKV_WPE_B128L 5
