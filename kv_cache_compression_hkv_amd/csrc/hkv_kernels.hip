@@ -243,8 +243,8 @@ struct StepMfmaAttn {
 };
 
 // Shape of the decode step per element type, head size and stream class C.
-// bf16 d128 has two: short streams (C = 0) run 8 waves/SIMD with 2 rows in
-// flight per lane, long streams (C = 1) 5 waves with 3; the host picks the class
+// bf16 d128 has two: short streams (C = 0) run 7 waves/SIMD, long streams
+// (C = 1) 5 waves, both with 3 rows in flight per lane; the host picks the class
 // from the configured budget.  C = 2 is the bf16 d64 eviction of the split
 // decode step, which has no matrix-core attention pass to take its tile from
 // and scores its slots from K like d128.
@@ -257,7 +257,7 @@ struct StepMfmaAttn {
 // per slot, in the same on-chip buffer).  Otherwise the tile and the positions
 // (36 bytes per slot) come from the attention (bf16 d64) or a vector-ALU pass
 // (fp32).  Sizes measured on MI355X: the d128 short-stream kernel's LDS stays
-// small enough for 8 workgroups per CU.
+// small enough for its 7 workgroups per CU (8 would fit too).
 #ifndef HKV_ONCHIP_KEYS
 #define HKV_ONCHIP_KEYS 1280
 #endif
