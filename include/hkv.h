@@ -272,7 +272,9 @@ hkv_status hkv_decode_step(const hkv_config *cfg, hkv_state *st, int32_t t,
  * table rows are spread over n_split workgroups (1 .. 8) that each leave a
  * partial softmax state in the state's workspace; a second kernel on `stream`
  * merges them into the output, writes the stream metadata back and runs the
- * eviction of due Global streams.  Arguments, layouts, outputs and errors are
+ * eviction of due Global streams (bf16: each split scores its own slots on
+ * the way, so that the second kernel only finishes the keys and selects;
+ * the workspace holds those scores).  Arguments, layouts, outputs and errors are
  * those of hkv_decode_step, and so are the results except for the order of
  * floating-point sums (outputs agree to rounding; a decision changes only where
  * two scores lie that close).  Calls on one state must not overlap: the

@@ -84,6 +84,18 @@ constexpr int kNT = kNW * kWave;
 #ifndef HKV_UER_L
 #define HKV_UER_L 2
 #endif
+// The split decode step's attention kernel: row fragments in flight per lane
+// and occupancy (0: those of the fused step), key tiles in flight in its
+// scoring pass.  Its grids hold a few workgroups per compute unit.
+#ifndef HKV_U_SPLIT
+#define HKV_U_SPLIT 0
+#endif
+#ifndef HKV_WPE_SPLIT
+#define HKV_WPE_SPLIT 0
+#endif
+#ifndef HKV_UE_SPLIT
+#define HKV_UE_SPLIT 1
+#endif
 template <int V>
 struct Int {
   static constexpr int value = V;
@@ -350,12 +362,15 @@ template <class T, int D, int C, bool AP>
 __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x, Scratch sc,
                                             EvictShared& es, uint64_t* skeys, bool tile_ready,
                                             uint2* qs, bool q_staged, bool cur_known,
-                                            float cur_m, float cur_il, const float4* ring_lds) {
+                                            float cur_m, float cur_il, const float4* ring_lds,
+                                            bool split_scores = false) {
   // (returns the number of freed slots: M, or 0 if nothing was evicted; skeys:
   // on-chip room for kNT keys, free once the eviction starts; es.cnt zeroed
   // by the caller before a barrier; cur_known: this launch's attention gave
   // the current query's softmax max cur_m and 1/sum cur_il; ring_lds: the
-  // stream's ring row staged on chip before a barrier, or null)
+  // stream's ring row staged on chip before a barrier, or null; split_scores
+  // (bf16): the split decode step's workgroups left each slot's partial score
+  // and current-query logit in the workspace, see k_split_attn)
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -410,9 +425,9 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
       }
     }
     const bool ring = HKV_RING && window && __ballot(!rok) == 0;   // (the same in every wave)
-    const bool one_pass = window && !ring && c <= OC::kOnePass;
+    const bool one_pass = window && !split_scores && !ring && c <= OC::kOnePass;
     keys_in_scratch = !one_pass;
-    if (window) {
+    if (window && !split_scores) {
       // v_mfma_f32_16x16x32_bf16: A = the W queries (rows W..15 zero), B = 16
       // keys per tile, K = 32 head elements per instruction; lane l holds A row
       // l%16 and B column l%16 at elements (l/16)*8 .. +7, and receives D rows
@@ -583,14 +598,27 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
           tiles(Int<OC::kTilesInFlight>{}, key_of);
       }
     } else {
+      // keys from the split workgroups' scores (the current query's share
+      // added here, with its merged max and sum), or from the state's scores
       __syncthreads();                 // subset counters zeroed before any wave adds
       for (int j0 = wave * kWave; j0 < c; j0 += kNT) {
         const int j = j0 + lane;
         const bool own = j < c;
-        const bool fresh = AP && j == slot_new;
-        const int pj = own ? (fresh ? t : a.pos[base + j]) : 0;
+        int pj = 0;
+        float sv = 0.f;
+        if (own) {
+          if (split_scores) {
+            const float2 v = reinterpret_cast<const float2*>(a.ws_tile + base * W)[j];
+            pj = a.ws_pos[base + j];
+            sv = v.x + exp2f(v.y - (cur_m - __log2f(cur_il)));   // (log2 of 2^max * sum)
+          } else {
+            const bool fresh = AP && j == slot_new;
+            pj = fresh ? t : a.pos[base + j];
+            sv = fresh ? 0.0f : a.score[base + j];
+          }
+        }
         const int sb = sub_of(pj);
-        if (own) sc.keys[j] = make_skey(sb, fresh ? 0.0f : a.score[base + j], pj);
+        if (own) sc.keys[j] = make_skey(sb, sv, pj);
         nn += __popcll(__ballot(own && sb == 0));
         nf += __popcll(__ballot(own && sb == 1));
       }
@@ -1516,14 +1544,22 @@ __device__ __forceinline__ StreamMeta stream_meta(const StepArgs& a, int s) {
 }
 
 template <class T, int D, int C>
+struct SplitCfg {
+  static constexpr int kWaves = HKV_WPE_SPLIT ? HKV_WPE_SPLIT : StepCfg<T, D, C>::kWaves;
+  static constexpr int kRows = HKV_U_SPLIT ? HKV_U_SPLIT : StepCfg<T, D, C>::kRows;
+};
+
+template <class T, int D, int C>
 __global__ __launch_bounds__(kNT)
-__attribute__((amdgpu_waves_per_eu(StepCfg<T, D, C>::kWaves, StepCfg<T, D, C>::kWaves)))
+__attribute__((amdgpu_waves_per_eu(SplitCfg<T, D, C>::kWaves, SplitCfg<T, D, C>::kWaves)))
 void k_split_attn(StepArgs a, int n_split, float* part) {
   using F = Frag<T>;
   constexpr int VE = F::N, G = D / VE, R = kWave / G, ES = sizeof(T);
-  constexpr int U = StepCfg<T, D, C>::kRows;
+  constexpr int U = SplitCfg<T, D, C>::kRows;
   constexpr int PS = D + 4;                        // floats per partial state
   __shared__ CombineShared cs;
+  constexpr bool kScores = sizeof(T) == 2;         // bf16: the splits score their slots
+  __shared__ __align__(16) uint2 lds_qw[kScores ? kMaxWobs * QStage<D>::kPitch : 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = xcd_block(blockIdx.x, gridDim.x);
   const int s = a.s_begin + blk / n_split, p = blk % n_split;
@@ -1662,6 +1698,91 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
     ps[D] = Mx;
     ps[D + 1] = L;
   }
+
+  // A Global stream at its eviction point (bf16): this split scores its own
+  // slots for the eviction, so that k_combine_evict needs no pass over K.  The
+  // matrix cores form the window queries' logits over the split's rows; each
+  // slot keeps the probability mass of queries 0..W-2 (their softmax max and
+  // sum from the ring, each query over the slots whose position does not
+  // exceed its own) and the current query's logit, whose share needs the
+  // statistics merged over all splits.  Stale ring entries leave the scoring
+  // to k_combine_evict (it makes the same check).
+  if constexpr (kScores) {
+    const int W = a.W, t = a.t;
+    const bool due = m.glob && m.c == m.B + a.M && a.q_win != nullptr;
+    float qo_l = 0.f;                              // lane i < W-1: query i's log2(2^max * sum)
+    bool rok = true;
+    if (due && lane < W - 1) {
+      const int step = t - W + 1 + lane;
+      const float4 e = a.qstat[(long long)s * W + step % W];
+      rok = __float_as_int(e.z) == step;
+      qo_l = e.x - __log2f(e.y);
+    }
+    if (due && __ballot(!rok) == 0) {              // (the same in every wave)
+      typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      using QS = QStage<D>;
+      constexpr int KC = D / 32, QP = QS::kPitch;
+      if (QS::row(tid) < W) QS::store(lds_qw, tid, QS::load(a.q_win, (long long)s * a.ld_qw, tid));
+      __syncthreads();
+      // v_mfma_f32_16x16x32_bf16: lane l holds A row (query) l%16 and B column
+      // (slot) l%16 at elements (l/16)*8 .. +7 of each 32-element chunk, and
+      // receives D rows (l/16)*4 .. +3 of slot column l%16
+      const int li = lane & 15, lk = lane >> 4;
+      float qo_r[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qo_r[r] = __shfl(qo_l, lk * 4 + r);
+      const int r0 = s0 * R, r1 = min(s1 * R, m.c);
+      const int nt = r1 > r0 ? (r1 - r0 + 15) / 16 : 0;
+      const char* krow_new = a.k_new + ((long long)s * a.ld_kv) * ES;
+      float* wsp = a.ws_tile + m.base * W;         // per slot: (partial score, current logit)
+      constexpr int UE = HKV_UE_SPLIT;
+      for (int kt0 = wave; kt0 < nt; kt0 += kNW * UE) {
+        uint4 kb[UE][KC];
+        int pj[UE];
+#pragma unroll
+        for (int u = 0; u < UE; ++u) {
+          const int j = r0 + (kt0 + u * kNW) * 16 + li;
+          const bool tile_in = kt0 + u * kNW < nt;   // uniform across the wave
+          const int jj = tile_in && j < r1 ? j : r0;
+          const bool fresh = jj == m.slot_new;       // (split 0 may not have stored it yet)
+          const char* row = fresh ? krow_new : a.k_pool + ((m.base + jj) * D) * ES;
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            kb[u][kc] = tile_in ? ld16(row + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
+          pj[u] = tile_in ? (fresh ? t : a.pos[m.base + jj]) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < UE; ++u) {
+          if (kt0 + u * kNW >= nt) break;                // uniform
+          const int j = r0 + (kt0 + u * kNW) * 16 + li;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            uint4 q = make_uint4(0, 0, 0, 0);
+            if (li < W) q = *reinterpret_cast<const uint4*>(lds_qw + li * QP + lk * 2 + kc * 8);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, q),
+                                                          __builtin_bit_cast(bf16x8, kb[u][kc]), acc, 0, 0, 0);
+          }
+          float pr = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = lk * 4 + r;
+            if (i < W - 1 && pj[u] <= t - W + 1 + i) pr += exp2f(acc[r] * a.scale_log2 - qo_r[r]);
+          }
+          pr += __shfl_xor(pr, 16);                 // rows 0-3 and 4-7
+          const int rc = (W - 1) & 3;
+          const float cv = rc == 0 ? acc[0] : rc == 1 ? acc[1] : rc == 2 ? acc[2] : acc[3];
+          const float cl = __shfl(cv * a.scale_log2, li + 16 * ((W - 1) >> 2));
+          if (lk == 0 && j < r1) {
+            wsp[2 * j] = pr;
+            wsp[2 * j + 1] = cl;
+            a.ws_pos[m.base + j] = pj[u];
+          }
+        }
+      }
+    }
+  }
 }
 
 template <class T, int D, int C>
@@ -1689,6 +1810,18 @@ __global__ __launch_bounds__(kNT) void k_combine_evict(StepArgs a, int n_split, 
   }
   const bool due = m.glob && m.c == m.B + a.M;
   if (due && tid < 2) es.cnt[tid] = 0;
+  // did the splits score the slots (bf16, window given, ring of queries
+  // 0..W-2 current: the check k_split_attn made)?
+  bool split_scores = false;
+  if (sizeof(T) == 2 && due && a.q_win != nullptr) {
+    bool rok = true;
+    const int lane = tid & 63;
+    if (lane < a.W - 1) {
+      const int step = a.t - a.W + 1 + lane;
+      rok = __float_as_int(a.qstat[(long long)s * a.W + step % a.W].z) == step;
+    }
+    split_scores = __ballot(!rok) == 0;
+  }
   // merge the partial states
   const float* ps = part + (long long)s * kMaxSplit * PS;
   float Mx = kNeg;
@@ -1722,11 +1855,11 @@ __global__ __launch_bounds__(kNT) void k_combine_evict(StepArgs a, int n_split, 
       Scratch sc{OC::kKeys ? reinterpret_cast<float*>(lds_keys) : lds_tile, lds_pos,
                  OC::kKeys ? lds_keys : nullptr};
       nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
-                                               Mx, cur_il, nullptr);
+                                               Mx, cur_il, nullptr, split_scores);
     } else {
       Scratch sc{a.ws_tile + m.base * a.W, a.ws_pos + m.base, a.ws_keys + m.base};
       nf_final = evict_stream<T, D, CE, false>(a, x, sc, es, skeys, false, lds_qw, false, true,
-                                               Mx, cur_il, nullptr);
+                                               Mx, cur_il, nullptr, split_scores);
     }
   } else if (a.log && tid < a.M) {
     a.log[(long long)s * a.M + tid] = -1;
