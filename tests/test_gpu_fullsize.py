@@ -182,3 +182,26 @@ def test_fullsize_per_layer_equals_folded(name):
     assert torch.equal(cap_f.view(torch.int16), cap_l.view(torch.int16))
     for a, b in zip(st_f, st_l):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["llamagen_xl_rho1_6", "janus_pro_1b_rho1_4"])
+def test_fullsize_split_step_parity(name):
+    """hkv_decode_step_split at full size, one launch pair per layer as a model
+    runs it: every eviction of the sampled groups is scored by the split
+    workgroups (bf16) and finished by the combine kernel; labels, layouts,
+    every eviction and every output agree with the oracle."""
+    w = WORKLOADS[name]
+    groups = sampled_groups(w)
+    print(f"[gpu] full-size split step {name}: S={w.S} N={w.N} groups={groups} n_split=2",
+          flush=True)
+    g = gpu_generation(w, SEED, group_streams(w, groups), per_layer=True, n_split=2)
+    torch.cuda.empty_cache()
+    rep = None
+    for (l, b) in groups:
+        rep = oracle_check_group(w, SEED, l, b, g, rep=rep)
+    print(f"  outputs {rep.outputs_checked} events {rep.events_checked} max err "
+          f"{rep.max_out_err:.3g} flags {rep.flagged_counts}/{rep.flagged_labels}/"
+          f"{rep.flagged_evictions}", flush=True)
+    assert not rep.failures, rep.failures[:8]
+    assert rep.events_checked > 0
+    assert rep.flagged_counts == rep.flagged_labels == rep.flagged_evictions == 0
