@@ -422,3 +422,27 @@ def test_split_step_rejects_bad_split():
             hk.hkv_decode_step_split(cfg, cache.state, w.P, buf, buf, w.head_dim, buf,
                                      w.q_rows * w.head_dim, buf, w.head_dim, None, 0, w.S, bad)
         assert e.value.status == hk.E_INVAL
+
+
+@pytest.mark.parametrize("dtype,head_dim,layers,batch,heads", [
+    ("bf16", 128, 3, 4, 50),     # 600 streams: 512 dealt to the XCDs in chunks of 64, 88 past them
+    ("bf16", 64, 3, 3, 7),       # 63 streams: contiguous runs per XCD, the first 7 runs one longer
+])
+def test_parity_xcd_mapping_tail(dtype, head_dim, layers, batch, heads):
+    """Stream counts that the workgroup-to-XCD mapping does not divide evenly:
+    every stream is still processed exactly once (first, middle and last
+    groups replayed on the oracle, lock-step scores)."""
+    w = small_config(dtype=dtype, head_dim=head_dim, layers=layers, batch=batch, heads=heads,
+                     image_tokens=60, prefill_image=20, rho=(1, 2), split_dist=12,
+                     local_window=8)
+    groups = sorted({(0, 0), (layers // 2, batch // 2), (layers - 1, batch - 1)})
+    print(f"[gpu] xcd mapping tail: S={w.S} d={head_dim} groups={groups}", flush=True)
+    g = gpu_generation(w, 0, group_streams(w, groups), score_trace=True)
+    rep = None
+    for (l, b) in groups:
+        rep = oracle_check_group(w, 0, l, b, g, rep=rep)
+    print(f"  outputs {rep.outputs_checked} events {rep.events_checked} max err "
+          f"{rep.max_out_err:.3g}", flush=True)
+    assert not rep.failures, rep.failures[:8]
+    assert rep.events_checked > 0 and rep.lockstep_events == rep.events_checked
+    assert rep.flagged_counts == rep.flagged_labels == rep.flagged_evictions == 0
