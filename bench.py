@@ -97,6 +97,32 @@ def step_bytes(labels, budgets, w):
     return out
 
 
+def attn_bytes(labels, budgets, w):
+    """Algorithmic bytes of every attention launch (hkv_decode_attn) of one
+    generation run as separate calls: per stream and step the K and V rows of
+    its c slots (2*d*e*c), query in and output out (2*d*e), the query-statistics
+    ring entry written (16) and 29 bytes of metadata read.  The append before it
+    and the eviction after it are separate launches."""
+    import numpy as np
+    d, e, M, P, T = w.head_dim, w.elem_bytes, w.evict_m, w.P, w.steps
+    row = d * e
+    one = lambda c: 2 * row * c + 2 * row + 16 + 29
+    out = np.zeros(T)
+    for lab, B in zip(labels.tolist(), budgets.tolist()):
+        steps = np.arange(P + 1, P + T + 1)
+        if lab == 2:
+            out += one(steps)
+        elif lab == 0:
+            out += one(np.minimum(steps, B))
+        else:
+            cnt = min(P, B)
+            for i in range(T):
+                c = cnt + 1
+                out[i] += one(c)
+                cnt = B if c == B + M else c
+    return out
+
+
 # ---------------------------------------------------------------- CPU baseline
 def _oracle_worker(args):
     """Runs the oracle on a list of (layer, sequence) groups, one after another;
@@ -145,9 +171,19 @@ def cpu_baseline(w, seed: int, max_groups_per_core: int = 36):
                 os.environ[k] = v
     wall = max(r[0] for r in res)
     n_groups = sum(r[1] for r in res)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     tokens = n_groups * w.steps / w.layers
     whole = "the whole workload" if n_groups == w.layers * w.batch else "a sample"
     return {"value": tokens / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "wall_s": round(wall, 2),
             "sample": f"{n_groups} of {w.layers * w.batch} (layer, sequence) groups of {w.name} "
                       f"({whole}), every decode step, numpy fp64, one process per core, "
                       f"{wall:.1f} s of oracle time on the busiest core"}
@@ -169,17 +205,27 @@ class Generation:
         self.qw = [self.Q.data_ptr() + (t - w.w_obs + 1 - (w.P - w.w_obs)) * d * eb
                    for t in range(w.N)]
 
-    def run(self, stream, events=None, capture=None):
+    def run(self, stream, events=None, capture=None, separate=False):
         """One generation; `events` = (start, end) recorded around the decode loop;
-        `capture` ([steps, S, d], untimed use only) receives every step's output."""
+        `capture` ([steps, S, d], untimed use only) receives every step's output;
+        `separate`: each decode step as its three calls (hkv_append,
+        hkv_decode_attn, hkv_ste_evict), which give the fused step's bits."""
         w, hk, st = self.w, self.hk, self.cache.state
-        d = w.head_dim
+        d, eb = w.head_dim, w.elem_bytes
         hk.hkv_classify(self.cfg, st, self.K, self.V, w.N * d, self.Q, w.q_rows * d, stream)
         if events is not None:
             events[0].record(stream)
         for t in range(w.P, w.N):
-            hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, self.qw[t],
-                               w.q_rows * d, self.out, d, None, 0, w.S, stream)
+            if separate:
+                q_cur = self.qw[t] + (w.w_obs - 1) * d * eb      # the query of position t
+                hk.hkv_append(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d, 0, w.S, stream)
+                hk.hkv_decode_attn(self.cfg, st, t, q_cur, w.q_rows * d, self.out, d, 0, w.S,
+                                   stream)
+                hk.hkv_ste_evict(self.cfg, st, t, self.qw[t], w.q_rows * d, None, 0, w.S,
+                                 stream)
+            else:
+                hk.hkv_decode_step(self.cfg, st, t, self.kp[t], self.vp[t], w.N * d,
+                                   self.qw[t], w.q_rows * d, self.out, d, None, 0, w.S, stream)
             if capture is not None:
                 capture[t - w.P].copy_(self.out)
         if events is not None:
@@ -330,7 +376,7 @@ def time_prefill(w, inputs, hk, full_cache_of, reps: int = 5) -> dict:
     return res
 
 
-def time_generations(gen_obj, steps, warmup):
+def time_generations(gen_obj, steps, warmup, separate=False):
     """Mean ms per generation over `steps` timed generations, and the mean
     duration of one decode-step launch (HIP events bracketing each generation's
     decode loop on the launch stream, divided by the launches; the short gaps
@@ -339,14 +385,14 @@ def time_generations(gen_obj, steps, warmup):
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        gen_obj.run(stream)
+        gen_obj.run(stream, separate=separate)
         gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state, stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        gen_obj.run(stream, evs[k])
+        gen_obj.run(stream, evs[k], separate=separate)
         # every generation's classification clears the device error word, so
         # each one is checked before the next starts
         gen_obj.hk.hkv_check(gen_obj.cfg, gen_obj.cache.state, stream)
@@ -360,6 +406,7 @@ def measure(w, inputs, hk, steps, warmup):
     """Timed generations of one workload: tokens/s over the whole generation
     and the dominant kernel's roofline figures (algorithmic bytes per launch /
     mean launch time from HIP events on the launch stream)."""
+    import numpy as np
     gen_obj = Generation(w, inputs, hk)
     ms, launch_ms = time_generations(gen_obj, steps, warmup)
     labels = gen_obj.cache.label.cpu().numpy()
@@ -369,11 +416,36 @@ def measure(w, inputs, hk, steps, warmup):
     achieved = float(alg.mean()) / kern_s / 1e9
     return gen_obj, {"value": round(w.batch * w.steps / (ms * 1e-3), 1), "unit": "tokens/s",
                      "ms_per_step": round(ms, 4), "mean_launch_us": round(kern_s * 1e6, 3),
+                     # the decode loop of each timed generation (HIP events): median, min
+                     "launch_us_median": round(float(np.median(launch_ms)) * 1e3, 3),
+                     "launch_us_min": round(float(launch_ms.min()) * 1e3, 3),
                      "alg_bytes_per_launch": round(float(alg.mean()), 1),
                      "achieved_GBs": round(achieved, 1),
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "labels": {"local": int((labels == 0).sum()),
                                 "global": int((labels == 1).sum())}}
+
+
+def levels(gen_obj, steps):
+    """The decode step measured at its two levels: the fused launch (measured
+    above) and the same step as three separate calls, whose middle one is the
+    attention kernel alone.  HIP events bracket each generation's decode loop;
+    the per-kernel split of the separate calls comes from a kernel trace
+    (rocprofv3), since events around single launches would add their own gaps.
+    This reports the loop time per decode step and the attention launch's
+    algorithmic bytes, from which the trace's attention duration gives its
+    fraction of peak."""
+    w = gen_obj.w
+    ms, launch_ms = time_generations(gen_obj, steps, 1, separate=True)
+    labels = gen_obj.cache.label.cpu().numpy()
+    budgets = gen_obj.cache.budget.cpu().numpy()
+    a = attn_bytes(labels, budgets, w)
+    return {"separate_calls": {"ms_per_step": round(ms, 4),
+                               "us_per_decode_step": round(float(launch_ms.mean()) * 1e3, 3),
+                               "launches_per_decode_step": 3,
+                               "attn_alg_bytes_per_launch": round(float(a.mean()), 1),
+                               "attn_kernel": "k_step<AP=false, AT=true, EV=false> "
+                                              "(hkv_decode_attn)"}}
 
 
 def fidelity(comp, full):
@@ -466,6 +538,9 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="also time hkv_prefill (prefill attention with the classification as "
                          "its by-product) against hkv_classify")
+    ap.add_argument("--levels", action="store_true",
+                    help="also time the decode step as three separate calls (append, "
+                         "attention, eviction): the attention kernel alone is the middle one")
     ap.add_argument("--e2e", action="store_true",
                     help="also time a random-weight transformer of the backbone's shape around "
                          "the decode path, compressed and full cache (bench_e2e.py)")
@@ -523,11 +598,15 @@ def main():
                      "traffic": traffic,
                      "kernel": "k_step (fused append + attention + STE)",
                      "mean_launch_us": m["mean_launch_us"],
+                     "launch_us_median": m["launch_us_median"],
+                     "launch_us_min": m["launch_us_min"],
                      "alg_bytes_per_launch": m["alg_bytes_per_launch"],
                      "copy_GBs": round(copy_gbs, 1),
                      "frac_of_copy": round(achieved / copy_gbs, 4)},
         "labels": m["labels"],
     }
+    if args.levels:
+        res["levels"] = levels(comp, max(2, args.steps // 2))
     if args.per_layer:
         splits = tuple(int(x) for x in args.per_layer_splits.split(",") if x)
         res["per_layer"] = time_per_layer(comp, max(2, args.steps // 2), splits)
