@@ -75,6 +75,11 @@ __device__ inline uint4 ld16_once(const void* p) {
 #endif
 }
 __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// Non-temporal store of a 16-byte fragment: the appended rows, scattered over
+// the pool one row per stream, are written past the caches' retention.
+__device__ inline void st16_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
 
 // ---------------------------------------------------------------- reductions
 template <int CTRL>
