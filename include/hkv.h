@@ -111,7 +111,13 @@ typedef struct {
 /* Cache state: device buffers owned by the caller (sizes from the helpers).
  * Index buffers must be aligned to their element size (label: 4 bytes). */
 typedef struct {
-  void    *k_pool, *v_pool;   /* [pool_slots, head_dim] element type           */
+  void    *k_pool, *v_pool;   /* one buffer [pool_slots, 2, head_dim] of the
+                               * element type: each slot's K row, then its V
+                               * row.  k_pool points at the buffer (slot 0's K
+                               * row), v_pool = k_pool + head_dim elements (slot
+                               * 0's V row); both rows of slot j are at
+                               * 2 * head_dim * j elements past them.  Any other
+                               * v_pool is rejected (HKV_E_INVAL).              */
   int32_t *pos;               /* [pool_slots] position held by each slot       */
   float   *score;             /* [pool_slots] STE scores at the last eviction  */
   int64_t *base;              /* [S] first pool slot of each stream            */

@@ -239,8 +239,11 @@ class HkvCache:
         self.cfg = cfg
         self.S = S
         self.slots = slots
-        self.k_pool = torch.zeros((slots, cfg.head_dim), dtype=dt, device=dev)
-        self.v_pool = torch.zeros((slots, cfg.head_dim), dtype=dt, device=dev)
+        # one pool buffer: each slot's K row, then its V row (k_pool and v_pool
+        # are views of it, as the C ABI requires)
+        self.kv_pool = torch.zeros((slots, 2, cfg.head_dim), dtype=dt, device=dev)
+        self.k_pool = self.kv_pool[:, 0]
+        self.v_pool = self.kv_pool[:, 1]
         self.pos = torch.full((slots,), -1, dtype=torch.int32, device=dev)
         self.score = torch.zeros((slots,), dtype=torch.float32, device=dev)
         self.base = torch.zeros((S,), dtype=torch.int64, device=dev)

@@ -109,6 +109,11 @@ hkv_status check_state_buffers(const hkv_config* c, const hkv_state* st, bool ne
   Derived d;
   hkv_status s = derive(c, &d);
   if (s != HKV_OK) return s;
+  // one pool buffer: slot j's K row, then its V row ([pool_slots, 2, head_dim])
+  const size_t row = size_t(c->head_dim) * (c->dtype == HKV_DT_BF16 ? 2 : 4);
+  if (static_cast<const char*>(st->v_pool) != static_cast<const char*>(st->k_pool) + row)
+    return fail(HKV_E_INVAL, "v_pool must be k_pool + head_dim elements (one [pool_slots, 2, "
+                "head_dim] buffer)");
   if (!need_workspace) return HKV_OK;
   if (!st->workspace || (reinterpret_cast<uintptr_t>(st->workspace) & 255u))
     return fail(HKV_E_INVAL, "workspace must be non-NULL and 256-byte aligned");

@@ -46,7 +46,8 @@ hkv_config base_cfg() {
 hkv_state fake_state(const hkv_config& c, int phase) {
   hkv_state st{};
   void* a = reinterpret_cast<void*>(uintptr_t(1) << 20);
-  st.k_pool = st.v_pool = a;
+  st.k_pool = a;   // one [pool_slots, 2, head_dim] buffer: V rows one K row later
+  st.v_pool = static_cast<char*>(a) + size_t(c.head_dim) * (c.dtype == HKV_DT_BF16 ? 2 : 4);
   st.pos = st.count = st.cap = st.budget = st.n_tokens = st.free_slots = st.n_free = st.err =
       static_cast<int32_t*>(a);
   st.score = st.qstat = static_cast<float*>(a);
@@ -135,6 +136,9 @@ int main() {
   hkv_state mis = st;
   mis.pos = reinterpret_cast<int32_t*>(uintptr_t(1) << 20 | 2);
   EXPECT(check_state_buffers(&c, &mis) == HKV_E_INVAL);
+  hkv_state apart = st;   // V rows not one K row after the K rows
+  apart.v_pool = st.k_pool;
+  EXPECT(check_state_buffers(&c, &apart) == HKV_E_INVAL);
   hkv_state nul{};
   EXPECT(check_state_buffers(&c, &nul) == HKV_E_INVAL);
   EXPECT(check_state_buffers(&c, nullptr) == HKV_E_INVAL);

@@ -82,6 +82,7 @@ def _fake_state(cfg, phase=1):
     a = 1 << 20
     st = hk.hkv_state(a, a, a, a, a, a, a, a, a, a, a, a, a, a, a, hk.hkv_workspace_bytes(cfg),
                       phase)
+    st.v_pool = a + cfg.head_dim * (2 if cfg.dtype == hk.DT_BF16 else 4)   # [slots, 2, d] pool
     return st
 
 
@@ -121,6 +122,13 @@ def test_entry_points_reject_before_launch():
     with pytest.raises(hk.HkvError) as e:
         hk.hkv_append(cfg, bad, 40, buf, buf, 64, 0, 16)
     assert e.value.status == hk.E_INVAL
+    # the pool is one [pool_slots, 2, head_dim] buffer: v_pool must follow k_pool by one row
+    for off in (0, 256, 64 * 2 + 16):
+        split = _fake_state(cfg)
+        split.v_pool = split.k_pool + off
+        with pytest.raises(hk.HkvError) as e:
+            hk.hkv_append(cfg, split, 40, buf, buf, 64, 0, 16)
+        assert e.value.status == hk.E_INVAL and "v_pool" in hk.hkv_last_error()
     small_ws = _fake_state(cfg)
     small_ws.workspace_bytes = 16
     with pytest.raises(hk.HkvError) as e:
