@@ -98,12 +98,12 @@ constexpr int kNT = kNW * kWave;
 #endif
 // Pool rows: each slot holds its K row and its V row side by side ([slot][2][D]
 // elements; v_pool = k_pool + D elements), so a slot's rows lie in one
-// 2*D-element span.  PRS is the pool's row stride in elements, for a kernel
-// templated on the head size D.  (The appended rows of a step, one slot per
-// stream scattered over the pool, are then written to one place per stream
-// instead of two: 1.2-1.7% faster per launch on the d128 workloads, the same
-// on LlamaGen-XL; measured on MI355X.)
-#define PRS (2 * D)
+// 2*D-element span; kPoolRow<D> is the pool's row stride in elements.  (The
+// appended rows of a step, one slot per stream scattered over the pool, are
+// then written to one place per stream instead of two: 1-2% faster per launch
+// on the d128 workloads, the same on LlamaGen-XL; measured on MI355X.)
+template <int D>
+constexpr int kPoolRow = 2 * D;
 template <int V>
 struct Int {
   static constexpr int value = V;
@@ -476,7 +476,7 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
             if (tile_in) {
               const int jj = vj[u] ? j : 0;
               const bool fresh = AP && jj == slot_new;
-              const char* row = fresh ? knew : a.k_pool + ((base + jj) * PRS) * ES;
+              const char* row = fresh ? knew : a.k_pool + ((base + jj) * kPoolRow<D>) * ES;
 #pragma unroll
               for (int kc = 0; kc < KC; ++kc) kb[u][kc] = ld16(row + (lk * 8 + kc * 32) * ES);
               pj[u] = fresh ? t : a.pos[base + jj];
@@ -670,13 +670,13 @@ __device__ __forceinline__ int evict_stream(const StepArgs& a, const StepCtx& x,
 #pragma unroll
           for (int e = 0; e < VE; ++e) qf[i][e] = tmp[e] * a.scale_log2;
         }
-        const char* kbase = a.k_pool + (base * PRS + sub * VE) * ES;
+        const char* kbase = a.k_pool + (base * kPoolRow<D> + sub * VE) * ES;
         const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
         for (int j0 = wave * R; j0 < c; j0 += kNW * R) {
           const int j = j0 + g;
           if (j < c) {
             float kf[VE];
-            F::to_f32(ld16((AP && j == slot_new) ? knew : kbase + (long long)j * PRS * ES), kf);
+            F::to_f32(ld16((AP && j == slot_new) ? knew : kbase + (long long)j * kPoolRow<D> * ES), kf);
             float mine = 0.f;
 #pragma unroll
             for (int i = 0; i < kMaxWobs; ++i) {
@@ -991,8 +991,8 @@ __device__ __forceinline__ void attend_mfma(const StepArgs& a, const StepCtx& x,
       const bool valid = (tt + u < t1) && j < c;
       const int jj = valid ? j : 0;              // branch-free: clamp, then zero
       const bool fresh = AP && jj == slot_new;
-      const char* kr = fresh ? knew : a.k_pool + (base + jj) * PRS * ES;
-      const char* vr = fresh ? vnew : a.v_pool + (base + jj) * PRS * ES;
+      const char* kr = fresh ? knew : a.k_pool + (base + jj) * kPoolRow<D> * ES;
+      const char* vr = fresh ? vnew : a.v_pool + (base + jj) * kPoolRow<D> * ES;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         kb[u][kc] = KC_ ? ld16(kr + (lk * 8 + kc * 32) * ES) : ld16_stream(kr + (lk * 8 + kc * 32) * ES);
@@ -1099,8 +1099,8 @@ __device__ __forceinline__ void rows_attend(int t0, int t1, int g, int ext, int 
       valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
       const int rr = valid[u] ? row : 0;
       const bool fresh = AP && rr == slot_new;
-      const char* kp = fresh ? knew : kbase + (long long)rr * PRS * ES;
-      const char* vp = fresh ? vnew : vbase + (long long)rr * PRS * ES;
+      const char* kp = fresh ? knew : kbase + (long long)rr * kPoolRow<D> * ES;
+      const char* vp = fresh ? vnew : vbase + (long long)rr * kPoolRow<D> * ES;
       kr[u] = cache_k ? ld16(kp) : ld16_stream(kp);
       vr[u] = cache_v ? ld16(vp) : ld16_stream(vp);
     }
@@ -1254,14 +1254,13 @@ void k_step(StepArgs a) {
   };
 
   // ---------------- append token t
-  // (The rows are written non-temporally: on Janus-Pro-7B's shape the append's
-  // scattered row writes cost about 7% of the launch, 0.7% less this way;
-  // measured on MI355X.)
+  // (The rows are written non-temporally: 0.8% faster per launch on Janus-Pro-7B's
+  // shape; measured on MI355X.)
   if (AP) {
     if (tid < 2 * G) {
       const bool isv = tid >= G;
       const int sb = tid % G;
-      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * PRS + sb * VE) * ES;
+      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * kPoolRow<D> + sb * VE) * ES;
       st16_stream(dst, app);
     }
     if (tid == 0) {
@@ -1319,8 +1318,8 @@ void k_step(StepArgs a) {
 #pragma unroll
       for (int i = 0; i < VE; ++i) qv[i] = qf[i] * a.scale_log2;
     }
-    const char* kbase = a.k_pool + (base * PRS + sub * VE) * ES;
-    const char* vbase = a.v_pool + (base * PRS + sub * VE) * ES;
+    const char* kbase = a.k_pool + (base * kPoolRow<D> + sub * VE) * ES;
+    const char* vbase = a.v_pool + (base * kPoolRow<D> + sub * VE) * ES;
     const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
     const char* vnew = a.v_new + ((long long)s * a.ld_kv + sub * VE) * ES;
 
@@ -1375,8 +1374,8 @@ void k_step(StepArgs a) {
           valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
           const int rr = valid[u] ? row : 0;
           const bool fresh = AP && rr == slot_new;
-          const char* kp = fresh ? knew : kbase + (long long)rr * PRS * ES;
-          const char* vp = fresh ? vnew : vbase + (long long)rr * PRS * ES;
+          const char* kp = fresh ? knew : kbase + (long long)rr * kPoolRow<D> * ES;
+          const char* vp = fresh ? vnew : vbase + (long long)rr * kPoolRow<D> * ES;
           kr[u] = cache_k ? ld16(kp) : ld16_stream(kp);
           vr[u] = ld16_stream(vp);
         }
@@ -1596,7 +1595,7 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
   if (p == 0) {                                    // append token t
     if (tid < 2 * G) {
       const bool isv = tid >= G;
-      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * PRS + (tid % G) * VE) * ES;
+      char* dst = (isv ? a.v_pool : a.k_pool) + ((base + slot_new) * kPoolRow<D> + (tid % G) * VE) * ES;
       st16_stream(dst, app);
     }
     if (tid == 0) {
@@ -1621,8 +1620,8 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
 #pragma unroll
     for (int i = 0; i < VE; ++i) qv[i] = qf[i] * a.scale_log2;
   }
-  const char* kbase = a.k_pool + (base * PRS + sub * VE) * ES;
-  const char* vbase = a.v_pool + (base * PRS + sub * VE) * ES;
+  const char* kbase = a.k_pool + (base * kPoolRow<D> + sub * VE) * ES;
+  const char* vbase = a.v_pool + (base * kPoolRow<D> + sub * VE) * ES;
   const char* knew = a.k_new + ((long long)s * a.ld_kv + sub * VE) * ES;
   const char* vnew = a.v_new + ((long long)s * a.ld_kv + sub * VE) * ES;
   float m_run = kNeg, l_run = 0.f;
@@ -1639,9 +1638,9 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
       valid[u] = (tt + u < t1) && row < ext && !(nf && is_free(row));
       const int rr = valid[u] ? row : 0;
       const bool fresh = rr == slot_new;
-      kr[u] = keep_k ? ld16(fresh ? knew : kbase + (long long)rr * PRS * ES)
-                     : ld16_stream(fresh ? knew : kbase + (long long)rr * PRS * ES);
-      vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * PRS * ES);
+      kr[u] = keep_k ? ld16(fresh ? knew : kbase + (long long)rr * kPoolRow<D> * ES)
+                     : ld16_stream(fresh ? knew : kbase + (long long)rr * kPoolRow<D> * ES);
+      vr[u] = ld16_stream(fresh ? vnew : vbase + (long long)rr * kPoolRow<D> * ES);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1757,7 +1756,7 @@ void k_split_attn(StepArgs a, int n_split, float* part) {
           const bool tile_in = kt0 + u * kNW < nt;   // uniform across the wave
           const int jj = tile_in && j < r1 ? j : r0;
           const bool fresh = jj == m.slot_new;       // (split 0 may not have stored it yet)
-          const char* row = fresh ? krow_new : a.k_pool + ((m.base + jj) * PRS) * ES;
+          const char* row = fresh ? krow_new : a.k_pool + ((m.base + jj) * kPoolRow<D>) * ES;
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc)
             kb[u][kc] = tile_in ? ld16(row + (lk * 8 + kc * 32) * ES) : make_uint4(0, 0, 0, 0);
@@ -2443,7 +2442,7 @@ __global__ __launch_bounds__(kNT) void k_layout(LayoutArgs a) {
     const bool isv = r >= G;
     const int sub = r % G;
     const char* src = (isv ? vs : ks) + ((long long)j * D + sub * VE) * ES;
-    st16((isv ? a.v_pool : a.k_pool) + ((base + to) * PRS + sub * VE) * ES, ld16(src));
+    st16((isv ? a.v_pool : a.k_pool) + ((base + to) * kPoolRow<D> + sub * VE) * ES, ld16(src));
   }
   for (int j = tid; j < P; j += kNT) {
     const int to = full ? j : dest[j];
